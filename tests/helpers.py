@@ -1,0 +1,61 @@
+"""Small helpers shared by the tests: tensor <-> numpy views of workloads.
+
+No layer arithmetic lives here; the oracle and the library each do their own.
+"""
+
+import numpy as np
+import torch
+
+from moe_layer_05_amd import workloads
+
+
+def np_f32(t):
+    """float32 numpy copy of a tensor (bfloat16 values are exact in float32)."""
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def np_u8(t):
+    return t.detach().to("cpu").view(torch.uint8).numpy()
+
+
+class LazyExperts:
+    """Indexable expert weights for the oracle: copies one expert to the host
+    when it is asked for, so a large device tensor never lands on the host
+    whole."""
+
+    def __init__(self, t):
+        self.t = t
+        self.fp8 = t.dtype == torch.uint8
+
+    def __getitem__(self, e):
+        w = self.t[int(e)]
+        return np_u8(w) if self.fp8 else np_f32(w)
+
+    def __len__(self):
+        return self.t.shape[0]
+
+
+def oracle_inputs(weights, tokens):
+    """Arguments of oracle.moe.moe_forward for a workload."""
+    fp8 = weights["wdtype"] == "fp8"
+    kw = dict(
+        x=np_f32(tokens["x"]),
+        logits=np_f32(tokens["logits"]),
+        w13=LazyExperts(weights["w13"]),
+        w2=LazyExperts(weights["w2"]),
+        wdtype="fp8" if fp8 else "float",
+    )
+    if fp8:
+        kw["w13_scale"] = np_f32(weights["w13_scale"])
+        kw["w2_scale"] = np_f32(weights["w2_scale"])
+    return kw
+
+
+def tiny_case(wdtype="float32", T=4, seed=0, device="cpu", **over):
+    cfg = workloads.CONFIGS["tiny"]
+    if over:
+        from dataclasses import replace
+        cfg = replace(cfg, **over)
+    w = workloads.make_weights(cfg, seed=seed, device=device, wdtype=wdtype)
+    tk = workloads.make_tokens(cfg, T, seed=seed, device=device)
+    return cfg, w, tk

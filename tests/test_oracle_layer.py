@@ -1,0 +1,247 @@
+"""Pins of the oracle's layer forward (float and FP8 modes).
+
+Compared with: a hand-derived example (tests/golden/hand_example.json), the
+dense "run every expert and mask" formulation, the full softmax mixture at
+K = E, the textbook SwiGLU FFN at E = K = 1 (torch library routines), exact
+invariants (zero input, token independence, scaling, expert relabelling) and
+the E4M3 error bound for the FP8 intermediate.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from scipy.special import softmax
+
+from oracle import fp8, moe
+from tests.helpers import np_f32, np_u8, oracle_inputs, tiny_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+def _num(v):
+    if isinstance(v, str):
+        return {"ln3": math.log(3.0), "-ln3/2": -math.log(3.0) / 2,
+                "-3ln3/8": -3 * math.log(3.0) / 8}[v]
+    return float(v)
+
+
+def _arr(x):
+    if isinstance(x, list):
+        return np.array([_arr(v) for v in x], dtype=np.float64)
+    return _num(x)
+
+
+def test_hand_example():
+    g = json.load(open(GOLDEN))
+    x = _arr(g["x"]).astype(np.float32)
+    lg = _arr(g["logits"]).astype(np.float32)
+    w13, w2 = _arr(g["w13"]), _arr(g["w2"])
+    _, parts = moe.moe_forward(x, lg, w13, w2, g["K"], return_parts=True)
+    assert parts["ids"].tolist() == g["ids"]
+    # logits are float32 (ln3 rounds), so weights and y match to ~1e-7
+    assert np.allclose(parts["weights"], g["weights"], atol=1e-7)
+    assert np.allclose(parts["y"], _arr(g["y"]), atol=1e-6)
+    y_dense = moe.moe_dense(x, lg, w13, w2, g["K"])
+    assert np.allclose(y_dense, _arr(g["y"]), atol=1e-6)
+
+
+def _float_case(T=4, seed=0, **over):
+    cfg, w, tk = tiny_case("float32", T=T, seed=seed, **over)
+    return cfg, oracle_inputs(w, tk)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_sparse_equals_dense(renorm):
+    cfg, kw = _float_case(T=6)
+    _, parts = moe.moe_forward(K=cfg.K, renormalize=renorm, return_parts=True, **kw)
+    yd = moe.moe_dense(K=cfg.K, renormalize=renorm, **kw)
+    assert np.allclose(parts["y"], yd, rtol=1e-12, atol=1e-14)
+
+
+def _expert_swiglu_torch(x, W13, W2):
+    """Textbook SwiGLU FFN W2 (silu(W1 x) * W3 x) with torch (float64)."""
+    I = W13.shape[0] // 2
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    W13t = torch.from_numpy(np.asarray(W13, np.float64))
+    h = F.silu(F.linear(xt, W13t[:I])) * F.linear(xt, W13t[I:])
+    return F.linear(h, torch.from_numpy(np.asarray(W2, np.float64))).numpy()
+
+
+def test_full_softmax_mixture_at_K_equals_E():
+    cfg, kw = _float_case(T=5)
+    _, parts = moe.moe_forward(K=cfg.E, return_parts=True, **kw)
+    p = softmax(kw["logits"].astype(np.float64), axis=1)
+    ref = np.zeros_like(parts["y"])
+    for e in range(cfg.E):
+        ref += p[:, e:e + 1] * _expert_swiglu_torch(kw["x"], kw["w13"][e], kw["w2"][e])
+    assert np.allclose(parts["y"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_single_expert_is_swiglu():
+    cfg, w, tk = tiny_case("float32", T=3, E=1, K=1)
+    kw = oracle_inputs(w, tk)
+    _, parts = moe.moe_forward(K=1, return_parts=True, **kw)
+    ref = _expert_swiglu_torch(kw["x"], kw["w13"][0], kw["w2"][0])
+    assert np.allclose(parts["y"], ref, rtol=1e-12, atol=1e-13)
+    assert (parts["weights"] == 1.0).all()
+
+
+@pytest.mark.parametrize("wdtype", ["float32", "fp8"])
+def test_zero_input_gives_zero(wdtype):
+    cfg, w, tk = tiny_case(wdtype)
+    tk["x"] = torch.zeros_like(tk["x"])
+    out = moe.moe_forward(K=cfg.K, **oracle_inputs(w, tk))
+    assert (out == 0).all()
+
+
+def test_token_independence_float():
+    cfg, kw = _float_case(T=5)
+    _, full = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    for t in range(5):
+        one = dict(kw, x=kw["x"][t:t + 1], logits=kw["logits"][t:t + 1])
+        _, p1 = moe.moe_forward(K=cfg.K, return_parts=True, **one)
+        # equal up to float64 rounding (BLAS blocks differently per batch)
+        assert np.allclose(p1["y"][0], full["y"][t], rtol=1e-13, atol=1e-15)
+    # sampled tokens give the same rows
+    _, sub = moe.moe_forward(K=cfg.K, tokens=[3, 1], return_parts=True, **kw)
+    assert np.allclose(sub["y"], full["y"][[3, 1]], rtol=1e-13, atol=1e-15)
+
+
+def test_scaling_w2_doubles_output():
+    cfg, kw = _float_case()
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    kw2 = dict(kw, w2=np.stack([kw["w2"][e] * 2 for e in range(cfg.E)]))
+    _, p2 = moe.moe_forward(K=cfg.K, return_parts=True, **kw2)
+    assert np.array_equal(p2["y"], 2 * p["y"])
+    # FP8: doubling the per-expert scale doubles the output exactly
+    cfg, w, tk = tiny_case("fp8")
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    _, p2 = moe.moe_forward(K=cfg.K, return_parts=True, **dict(kw, w2_scale=kw["w2_scale"] * 2))
+    assert np.array_equal(p2["y"], 2 * p["y"])
+
+
+@pytest.mark.parametrize("wdtype", ["float32", "fp8"])
+def test_expert_relabelling_invariance(wdtype):
+    cfg, w, tk = tiny_case(wdtype, T=6)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    perm = np.random.default_rng(1).permutation(cfg.E)
+    kwp = dict(kw)
+    kwp["logits"] = kw["logits"][:, perm]
+    kwp["w13"] = np.stack([kw["w13"][e] for e in perm])
+    kwp["w2"] = np.stack([kw["w2"][e] for e in perm])
+    if wdtype == "fp8":
+        kwp["w13_scale"] = kw["w13_scale"][perm]
+        kwp["w2_scale"] = kw["w2_scale"][perm]
+    _, pp = moe.moe_forward(K=cfg.K, return_parts=True, **kwp)
+    assert np.array_equal(perm[pp["ids"]], p["ids"])
+    assert np.allclose(pp["y"], p["y"], rtol=1e-13, atol=1e-15)
+
+
+def test_float32_vs_float64_arithmetic():
+    cfg, kw = _float_case(T=4)
+    _, p64 = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    _, p32 = moe.moe_forward(K=cfg.K, return_parts=True, dtype=np.float32, **kw)
+    assert np.abs(p64["y"] - p32["y"]).max() <= 1e-5 * np.abs(p64["y"]).max()
+
+
+# ---------------------------------------------------------------- FP8 mode
+
+def test_fp8_sparse_equals_dense():
+    cfg, w, tk = tiny_case("fp8", T=6)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    yd = moe.moe_dense(K=cfg.K, **kw)
+    assert np.allclose(p["y"], yd, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_activation_scale_and_codes():
+    cfg, w, tk = tiny_case("fp8")
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    amax = np.float32(np.abs(kw["x"]).max())
+    assert p["s_x"] == np.float32(amax / np.float32(448.0))
+
+
+def test_fp8_unrouted_expert_has_no_effect():
+    cfg, w, tk = tiny_case("fp8", T=2)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    unrouted = sorted(set(range(cfg.E)) - set(p["ids"].ravel().tolist()))
+    assert unrouted
+    w13 = np.stack([kw["w13"][e] for e in range(cfg.E)])
+    sc = kw["w13_scale"].copy()
+    for e in unrouted:          # huge activations if it were ever evaluated
+        w13[e] = 0x7E
+        sc[e] = 1e3
+    _, p2 = moe.moe_forward(K=cfg.K, return_parts=True, **dict(kw, w13=w13, w13_scale=sc))
+    assert np.array_equal(p2["y"], p["y"]) and p2["s_a"] == p["s_a"]
+
+
+def test_fp8_up_projection_homogeneity():
+    """Doubling the up rows doubles a, so s_a doubles and the codes stay: y doubles."""
+    cfg, w, tk = tiny_case("fp8", T=4)
+    kw = oracle_inputs(w, tk)
+    I = cfg.I
+    w13 = np.stack([kw["w13"][e] for e in range(cfg.E)])
+    # give the up rows headroom (|v| <= 224, no subnormals) so doubling is exact
+    vals = fp8.decode(w13[:, I:])
+    vals = np.clip(vals, -224, 224)
+    vals[np.abs(vals) < 2.0 ** -6] = 0
+    w13[:, I:] = fp8.encode(vals)
+    assert np.array_equal(fp8.decode(w13[:, I:]), vals)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **dict(kw, w13=w13))
+    w13d = w13.copy()
+    w13d[:, I:] = fp8.encode(vals * 2)
+    assert np.array_equal(fp8.decode(w13d[:, I:]), vals * 2)
+    _, p2 = moe.moe_forward(K=cfg.K, return_parts=True, **dict(kw, w13=w13d))
+    assert p2["s_a"] == 2 * p["s_a"]
+    assert np.array_equal(p2["y"], 2 * p["y"])
+
+
+def test_fp8_intermediate_error_bound():
+    """y_fp8 differs from the unquantised-intermediate layer (same x^, W) by at
+    most the E4M3 half-ulp bound propagated through W2 and the weights."""
+    cfg, w, tk = tiny_case("fp8", T=4)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    # the same layer on dequantised float inputs: nothing is quantised there
+    qx, s_x = fp8.quantize(kw["x"])
+    xh = fp8.dequantize(qx, s_x)
+    w13f = np.stack([fp8.dequantize(kw["w13"][e], kw["w13_scale"][e]) for e in range(cfg.E)])
+    w2f = np.stack([fp8.dequantize(kw["w2"][e], kw["w2_scale"][e]) for e in range(cfg.E)])
+    _, pf = moe.moe_forward(xh, kw["logits"], w13f, w2f, cfg.K, return_parts=True)
+    s_a = float(p["s_a"])
+    bound = np.zeros_like(pf["y"])
+    for t in range(4):
+        for k in range(cfg.K):
+            e = p["ids"][t, k]
+            W13 = w13f[e]
+            g, u = W13[:cfg.I] @ xh[t], W13[cfg.I:] @ xh[t]
+            a = g / (1 + np.exp(-g)) * u
+            da = np.maximum(np.abs(a) * 2.0 ** -4, 2.0 ** -10 * s_a)
+            bound[t] += p["weights"][t, k] * (np.abs(w2f[e]) @ da)
+    err = np.abs(p["y"] - pf["y"])
+    assert (err <= bound * (1 + 1e-6) + 1e-12).all()
+    assert err.max() > 0                         # the intermediate was quantised
+
+
+def test_fp8_scale_is_per_call():
+    """One activation scale for the whole call: a token with tiny activations
+    next to a huge one is quantised coarsely, unlike when it runs alone."""
+    cfg, w, tk = tiny_case("fp8", T=2)
+    x = tk["x"].clone()
+    x[1] *= 2.0 ** -12
+    tk["x"] = x
+    kw = oracle_inputs(w, tk)
+    _, both = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    one = dict(kw, x=kw["x"][1:], logits=kw["logits"][1:])
+    _, alone = moe.moe_forward(K=cfg.K, return_parts=True, **one)
+    assert not np.allclose(both["y"][1], alone["y"][0], rtol=1e-3)
+    assert both["s_x"] > alone["s_x"]
