@@ -1,0 +1,189 @@
+/*
+ * moe.h -- C ABI of the fused Mixture-of-Experts layer forward for AMD MI355X
+ * (gfx950).  Library: moe_layer_05_amd/libmoemi.so.
+ *
+ * The layer (pages on "Mixture-of-Experts kernel engineering on Amazon
+ * SageMaker AI"): each token activates a few experts chosen by a router; the
+ * tokens are grouped by expert for grouped matrix products; each expert is a
+ * gated feed-forward network; the expert outputs are combined with the routing
+ * weights (toolboxkart.tech page, "Why MoE inference needs specialized
+ * kernels"; kongchang.com page, "Why MoE Inference Is So Sensitive to Kernel
+ * Engineering" and "Swap-AB"; aib.vote page, second and third paragraphs).
+ *
+ * Notation: T tokens, H hidden size, I intermediate size per expert, E
+ * experts, K experts per token.  A "pair" i = t*K + k is token t's k-th choice.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer to row-major contiguous memory,
+ *    owned by the caller.  The library allocates nothing, keeps no pointer
+ *    after a call returns, and is re-entrant (its only global state is a table
+ *    of device properties filled once per device).
+ *  - Every call enqueues its kernels on `stream` and returns at once; nothing
+ *    synchronises the host and nothing is read back to the host.
+ *  - All argument checks run on the host before any HIP call and look at
+ *    values only, never at tensor contents.  On any error nothing is enqueued.
+ *  - T == 0 is valid: MOE_OK with nothing enqueued.
+ *  - Non-finite logits or activations give undefined results.
+ *  - No code is compiled at run time: every shape is a kernel argument, so a
+ *    new token count never triggers a compilation (toolboxkart.tech page,
+ *    section 3 on repeated compilation; aib.vote page, fourth paragraph).
+ *  - A launch error is reported as MOE_ERR_HIP; device faults surface at the
+ *    caller's next synchronisation as HIP errors.
+ */
+#ifndef MOE_LAYER_05_AMD_MOE_H
+#define MOE_LAYER_05_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL                   */
+  MOE_ERR_SHAPE = 2,        /* a size is negative or inconsistent (K > E)   */
+  MOE_ERR_UNSUPPORTED = 3,  /* outside the supported range (see each call)  */
+  MOE_ERR_WORKSPACE = 4,    /* workspace smaller than the size query        */
+  MOE_ERR_HIP = 5           /* a HIP launch or runtime call failed          */
+} moe_status;
+
+typedef enum {
+  MOE_BF16 = 0,             /* expert weights are bfloat16                  */
+  MOE_FP8_E4M3 = 1          /* expert weights are OCP E4M3 codes + scales   */
+} moe_wdtype;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/*
+ * Router (a1).  For each token, the K largest of its E float32 logits, larger
+ * first; equal logits go to the lower expert id (+0.0 and -0.0 are equal).
+ * The choice is made on the logits themselves.  Weights:
+ *   renormalize != 0: w_k = exp(l_k - l_max) / sum_{j<K} exp(l_j - l_max)
+ *   renormalize == 0: w_k = softmax(l)_k over all E experts.
+ * A few experts per token, routed dynamically: toolboxkart.tech page, "Why MoE
+ * inference needs specialized kernels"; kongchang.com page, "Why MoE Inference
+ * Is So Sensitive to Kernel Engineering".
+ *
+ *   logits        [T, E] float32
+ *   topk_ids      [T, K] int32   (out)
+ *   topk_weights  [T, K] float32 (out)
+ * Supported: 1 <= K <= min(E, 64), E <= 1024.  16-byte alignment not needed.
+ */
+moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t K,
+                          int32_t renormalize, int32_t* topk_ids,
+                          float* topk_weights, hipStream_t stream);
+
+/*
+ * Align (a2).  Stable counting sort of the pairs i = t*K + k by expert:
+ * experts in ascending id; inside an expert ascending i; each expert's run
+ * padded with the sentinel T*K to a multiple of block_m; an expert with no
+ * pair takes no block.  This groups the tokens of each expert for the grouped
+ * products (kongchang.com page, "Swap-AB": grouped GEMMs; "Why MoE Inference Is
+ * So Sensitive...": the number of tokens per expert varies).
+ *
+ *   topk_ids      [T, K] int32, values in [0, E)
+ *   sorted_ids    [moe_align_capacity(...)] int32 (out); entries
+ *                 [0, *num_post_pad) are defined
+ *   block_expert  [moe_align_capacity(...) / block_m] int32 (out); entries
+ *                 [0, *num_post_pad / block_m) are defined
+ *   num_post_pad  [1] int32 (out): sum over experts of ceil(count/block_m)*block_m
+ *   workspace     device scratch of moe_align_workspace_bytes(...) bytes
+ * Supported: block_m in {16, 32, 64, 128, 256}; E <= 1024; T*K < 2^31.
+ */
+size_t moe_align_capacity(int64_t T, int32_t K, int32_t E, int32_t block_m);
+size_t moe_align_workspace_bytes(int64_t T, int32_t K, int32_t E, int32_t block_m);
+moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E,
+                     int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                     int32_t* num_post_pad, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Activation quantisation (a0, FP8 path).  Per-tensor E4M3:
+ *   scale = amax|x| / 448 (one float32 division; 1 when amax is 0)
+ *   codes[j] = E4M3(x[j] / scale), x[j] / scale an IEEE float32 division,
+ *   rounded to nearest even, saturated to +-448, sign kept.
+ * FP8 E4M3 with a per-tensor scale: kongchang.com page, FP8 explainer under
+ * "Triton Backend Routing"; aib.vote page, third paragraph.
+ *
+ *   x          [n] bfloat16 (raw 16-bit patterns), 16-byte aligned
+ *   codes      [n] uint8 (out)
+ *   scale      [1] float32 (out)
+ *   workspace  >= moe_act_quant_workspace_bytes() bytes of device scratch
+ * Supported: n % 8 == 0.
+ */
+size_t moe_act_quant_workspace_bytes(void);
+moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes,
+                             float* scale, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Fused layer forward (a0..a6).  out[t] = bfloat16_rne( sum_k w[t,k] *
+ *   W2_e (silu(W1_e x^_t) * (W3_e x^_t)) ),  e = topk_ids[t,k],
+ * with W1_e = w13[e, 0:I, :] (gate) and W3_e = w13[e, I:2I, :] (up).
+ * The routing, the grouping of tokens by expert, the grouped products, the
+ * scaling and the weighted aggregation all run on the device
+ * (toolboxkart.tech page, "Why MoE inference needs specialized kernels": a
+ * fused kernel combines routing, data movement and expert math; aib.vote
+ * page, third paragraph: scaling, products and expert aggregation in one pass).
+ * For thin token batches the expert weight rows take the row side of the
+ * matrix instructions (the Swap-AB idea: toolboxkart.tech page, section 1;
+ * kongchang.com page, "Swap-AB"; aib.vote page, second paragraph).
+ *
+ * MOE_BF16:     x^ = x; weights bfloat16.
+ * MOE_FP8_E4M3: x^ = dequantised per-tensor E4M3 of x (as moe_act_quant_fp8);
+ *               W = code * w13_scale[e] (or w2_scale[e]); the intermediate
+ *               a = silu(g) * u is quantised per tensor over all pairs, from
+ *               its float32 value, before the down projection.
+ *
+ * Fields:
+ *   x               [T, H] bfloat16
+ *   router_logits   [T, E] float32
+ *   w13             [E, 2I, H] bfloat16 or uint8 E4M3 codes
+ *   w2              [E, H, I]  bfloat16 or uint8 E4M3 codes
+ *   w13_scale, w2_scale  [E] float32, FP8 only (ignored for bf16, may be NULL)
+ *   out             [T, H] bfloat16 (out)
+ *   topk_ids_out    [T, K] int32 (out, optional: NULL to skip)
+ *   topk_weights_out[T, K] float32 (out, optional: NULL to skip)
+ *   workspace       device scratch, >= moe_fused_workspace_bytes(args) bytes,
+ *                   16-byte aligned; its contents on entry do not matter
+ * Supported: H % 16 == 0, I % 16 == 0, 1 <= K <= min(E, 64), E <= 1024,
+ * T*K < 2^31; x, w13, w2, out and workspace 16-byte aligned.
+ */
+typedef struct {
+  moe_wdtype wdtype;
+  int64_t T;
+  int32_t H, I, E, K;
+  int32_t renormalize;
+  const void* x;
+  const float* router_logits;
+  const void* w13;
+  const void* w2;
+  const float* w13_scale;
+  const float* w2_scale;
+  void* out;
+  int32_t* topk_ids_out;
+  float* topk_weights_out;
+  void* workspace;
+  size_t workspace_bytes;
+} moe_fused_args;
+
+/* Workspace bytes moe_fused_forward needs for the shape in *args (pointers
+ * are not read). 0 when the shape is invalid. */
+size_t moe_fused_workspace_bytes(const moe_fused_args* args);
+
+/* Block size (tokens per expert block) moe_fused_forward uses for this shape;
+ * moe_align with this block_m reproduces its layout. */
+int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                          moe_wdtype wdtype);
+
+moe_status moe_fused_forward(const moe_fused_args* args, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_05_AMD_MOE_H */

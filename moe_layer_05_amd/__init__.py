@@ -1,5 +1,19 @@
 """Fused Mixture-of-Experts layer forward for AMD MI355X (gfx950).
 
-The compute path is a HIP library with a C ABI (``include/moe.h``); this
-package is its thin Python binding plus the seeded synthetic workloads.
+The compute path is the HIP library libmoemi.so with the C ABI of
+``include/moe.h``; this package is its thin Python binding (``binding``), the
+ahead-of-time build (``build``) and the seeded synthetic workloads
+(``workloads``).  The library is loaded on first use; there is no fallback.
 """
+
+from .binding import (  # noqa: F401
+    FusedMoE,
+    MoEError,
+    act_quant_fp8,
+    align,
+    align_capacity,
+    fused_block_m,
+    fused_forward,
+    lib,
+    route_topk,
+)

@@ -1,0 +1,257 @@
+"""ctypes binding of libmoemi.so (C ABI in include/moe.h).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the layer runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoemi.so")
+
+MOE_BF16 = 0
+MOE_FP8_E4M3 = 1
+
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
+          4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+
+
+class FusedArgs(ctypes.Structure):
+    _fields_ = [
+        ("wdtype", ctypes.c_int),
+        ("T", ctypes.c_int64),
+        ("H", ctypes.c_int32),
+        ("I", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("K", ctypes.c_int32),
+        ("renormalize", ctypes.c_int32),
+        ("x", ctypes.c_void_p),
+        ("router_logits", ctypes.c_void_p),
+        ("w13", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("w13_scale", ctypes.c_void_p),
+        ("w2_scale", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("topk_ids_out", ctypes.c_void_p),
+        ("topk_weights_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+_SIGS = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route_topk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "moe_align_capacity": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32]),
+    "moe_align_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.c_int32]),
+    "moe_align": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]),
+    "moe_act_quant_workspace_bytes": (ctypes.c_size_t, []),
+    "moe_act_quant_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]),
+    "moe_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FusedArgs)]),
+    "moe_fused_block_m": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int]),
+    "moe_fused_forward": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p]),
+}
+
+
+def lib():
+    """The loaded library; raises if it is not built (no fallback exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m moe_layer_05_amd.build`; "
+                "this package has no non-HIP fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        raise MoEError(status, what)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+# ------------------------------------------------------------------ a1
+
+def route_topk(logits, K, renormalize=True, stream=None):
+    """(topk_ids [T, K] int32, topk_weights [T, K] float32) of [T, E] logits."""
+    T, E = logits.shape
+    lp = _dev(logits, torch.float32, "logits")
+    ids = torch.empty(T, K, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, K, dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route_topk(lp, T, E, K, int(bool(renormalize)), _ptr(ids), _ptr(w),
+                                _stream(stream)), "moe_route_topk")
+    return ids, w
+
+
+# ------------------------------------------------------------------ a2
+
+def align_capacity(T, K, E, block_m):
+    return int(lib().moe_align_capacity(T, K, E, block_m))
+
+
+def align(topk_ids, E, block_m, stream=None):
+    """(sorted_ids, block_expert, num_post_pad [1] int32) of [T, K] ids.
+    Only sorted_ids[:num_post_pad] and block_expert[:num_post_pad // block_m]
+    are defined."""
+    T, K = topk_ids.shape
+    ip = _dev(topk_ids, torch.int32, "topk_ids")
+    L = lib()
+    cap = int(L.moe_align_capacity(T, K, E, block_m))
+    if cap == 0 and T > 0:
+        raise MoEError(3, "moe_align_capacity")
+    dev = topk_ids.device
+    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // max(block_m, 1), 1), dtype=torch.int32, device=dev)
+    npp = torch.zeros(1, dtype=torch.int32, device=dev)
+    wsb = int(L.moe_align_workspace_bytes(T, K, E, block_m))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    _check(L.moe_align(ip, T, K, E, block_m, _ptr(sorted_ids), _ptr(block_expert), _ptr(npp),
+                       _ptr(ws), wsb, _stream(stream)), "moe_align")
+    return sorted_ids, block_expert, npp
+
+
+# ------------------------------------------------------------------ a0
+
+def act_quant_fp8(x, stream=None):
+    """(codes uint8 shaped like x, scale [1] float32) of bfloat16 x."""
+    xp = _dev(x, torch.bfloat16, "x")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty(1, dtype=torch.float32, device=x.device)
+    L = lib()
+    wsb = int(L.moe_act_quant_workspace_bytes())
+    ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _check(L.moe_act_quant_fp8(xp, x.numel(), _ptr(codes), _ptr(scale), _ptr(ws), wsb,
+                               _stream(stream)), "moe_act_quant_fp8")
+    return codes, scale
+
+
+# ------------------------------------------------------------------ a0..a6
+
+def fused_block_m(T, H, I, E, K, fp8):
+    return int(lib().moe_fused_block_m(T, H, I, E, K, MOE_FP8_E4M3 if fp8 else MOE_BF16))
+
+
+class FusedMoE:
+    """The fused layer forward bound to fixed weights.
+
+    w13 [E, 2I, H] and w2 [E, H, I] are bfloat16, or uint8 E4M3 codes with
+    w13_scale / w2_scale [E] float32.  The workspace is a torch buffer grown
+    on demand and reused across calls (the library allocates nothing)."""
+
+    def __init__(self, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True):
+        self.fp8 = w13.dtype == torch.uint8
+        self.E, twoI, self.H = w13.shape
+        self.I = twoI // 2
+        self.K = K
+        self.renormalize = renormalize
+        self.w13 = w13
+        self.w2 = w2
+        want = torch.uint8 if self.fp8 else torch.bfloat16
+        _dev(w13, want, "w13")
+        _dev(w2, want, "w2")
+        if tuple(w2.shape) != (self.E, self.H, self.I):
+            raise ValueError("w2 must be [E, H, I]")
+        if self.fp8:
+            _dev(w13_scale, torch.float32, "w13_scale")
+            _dev(w2_scale, torch.float32, "w2_scale")
+        self.w13_scale = w13_scale
+        self.w2_scale = w2_scale
+        self._ws = None
+
+    def args(self, x, logits, out, ids=None, wts=None):
+        a = FusedArgs()
+        a.wdtype = MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+        a.T = x.shape[0]
+        a.H, a.I, a.E, a.K = self.H, self.I, self.E, self.K
+        a.renormalize = int(bool(self.renormalize))
+        a.x = _dev(x, torch.bfloat16, "x").value
+        a.router_logits = _dev(logits, torch.float32, "logits").value
+        a.w13 = self.w13.data_ptr()
+        a.w2 = self.w2.data_ptr()
+        a.w13_scale = self.w13_scale.data_ptr() if self.fp8 else None
+        a.w2_scale = self.w2_scale.data_ptr() if self.fp8 else None
+        a.out = _dev(out, torch.bfloat16, "out").value
+        a.topk_ids_out = ids.data_ptr() if ids is not None else None
+        a.topk_weights_out = wts.data_ptr() if wts is not None else None
+        return a
+
+    def workspace_bytes(self, T):
+        a = FusedArgs()
+        a.wdtype = MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+        a.T, a.H, a.I, a.E, a.K = T, self.H, self.I, self.E, self.K
+        return int(lib().moe_fused_workspace_bytes(ctypes.byref(a)))
+
+    def workspace(self, T, device):
+        need = self.workspace_bytes(T)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        return self._ws
+
+    def __call__(self, x, logits, out=None, return_topk=False, stream=None):
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty(T, self.H, dtype=torch.bfloat16, device=x.device)
+        ids = wts = None
+        if return_topk:
+            ids = torch.empty(T, self.K, dtype=torch.int32, device=x.device)
+            wts = torch.empty(T, self.K, dtype=torch.float32, device=x.device)
+        ws = self.workspace(T, x.device)
+        a = self.args(x, logits, out, ids, wts)
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
+        _check(lib().moe_fused_forward(ctypes.byref(a), _stream(stream)), "moe_fused_forward")
+        return (out, ids, wts) if return_topk else out
+
+
+def fused_forward(x, logits, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True,
+                  return_topk=False, stream=None):
+    """One-shot fused forward (allocates its workspace through torch)."""
+    m = FusedMoE(w13, w2, K, w13_scale, w2_scale, renormalize)
+    return m(x, logits, return_topk=return_topk, stream=stream)

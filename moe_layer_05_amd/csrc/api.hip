@@ -1,0 +1,267 @@
+// C ABI of the fused MoE layer (declared in include/moe.h): host-side argument
+// checks, workspace layout and the launch sequence.  No device memory is
+// allocated and nothing synchronises the host.
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlignBytes = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+
+size_t round_up(size_t x) { return (x + kAlignBytes - 1) / kAlignBytes * kAlignBytes; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute-unit count of the current device, filled once per device.
+int num_cus() {
+  static std::mutex mu;
+  static int cache[256] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+bool block_m_ok(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+// Upper bound of the number of blocks of the aligned layout: each active
+// expert adds at most one partly filled block, and at most min(E, P) experts
+// are active.
+int64_t max_blocks(int64_t P, int E, int bm) {
+  const int64_t active = P < E ? P : E;
+  return P / bm + active;
+}
+
+struct FusedLayout {
+  size_t ids, wts, sorted, bexp, npp, rank, scal, qx, a, qa, dw, total;
+  int bm;
+  int64_t cap, nblk;
+};
+
+FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
+  FusedLayout L{};
+  const int64_t P = T * K;
+  const bool fp8 = wd == MOE_FP8_E4M3;
+  L.bm = moe_fused_block_m(T, H, I, E, K, wd);
+  L.nblk = max_blocks(P, E, L.bm);
+  L.cap = L.nblk * L.bm;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
+  L.ids = take(P * 4);
+  L.wts = take(P * 4);
+  L.sorted = take(L.cap * 4);
+  L.bexp = take(L.nblk * 4);
+  L.npp = take(4);
+  L.rank = take(P * 4);
+  L.scal = take(2 * 4);
+  L.qx = take(fp8 ? (size_t)T * H : 0);
+  L.a = take((size_t)P * I * (fp8 ? 4 : 2));
+  L.qa = take(fp8 ? (size_t)P * I : 0);
+  L.dw = take((size_t)P * H * 4);
+  L.total = off;
+  return L;
+}
+
+moe_status check_shape(int64_t T, int H, int I, int E, int K) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || K <= 0) return MOE_ERR_SHAPE;
+  if (K > E) return MOE_ERR_SHAPE;
+  if (E > kMaxE || K > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (H % 16 != 0 || I % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is negative or inconsistent";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported range";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP call failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t K,
+                          int32_t renormalize, int32_t* topk_ids, float* topk_weights,
+                          hipStream_t stream) {
+  if (T < 0 || E <= 0 || K <= 0) return MOE_ERR_SHAPE;
+  if (K > E) return MOE_ERR_SHAPE;
+  if (E > kMaxE || K > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  return hip_status(
+      launch_router(logits, T, E, K, renormalize, topk_ids, topk_weights, nullptr, 0, stream));
+}
+
+size_t moe_align_capacity(int64_t T, int32_t K, int32_t E, int32_t block_m) {
+  if (T < 0 || K <= 0 || E <= 0 || !block_m_ok(block_m)) return 0;
+  return (size_t)(max_blocks(T * K, E, block_m) * block_m);
+}
+
+size_t moe_align_workspace_bytes(int64_t T, int32_t K, int32_t E, int32_t block_m) {
+  if (T < 0 || K <= 0 || E <= 0 || !block_m_ok(block_m)) return 0;
+  return round_up((size_t)(T * K) * 4);
+}
+
+moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, int32_t block_m,
+                     int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || E <= 0 || K <= 0) return MOE_ERR_SHAPE;
+  if (K > E) return MOE_ERR_SHAPE;
+  if (E > kMaxE || !block_m_ok(block_m)) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)K >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (!num_post_pad) return MOE_ERR_NULL;
+  if (T > 0 && (!topk_ids || !sorted_ids || !block_expert || !workspace)) return MOE_ERR_NULL;
+  if (workspace_bytes < moe_align_workspace_bytes(T, K, E, block_m)) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_align(topk_ids, (int)(T * K), E, block_m, sorted_ids, block_expert,
+                                 num_post_pad, static_cast<int32_t*>(workspace), stream));
+}
+
+size_t moe_act_quant_workspace_bytes(void) { return kAlignBytes; }
+
+moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* scale,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n < 0) return MOE_ERR_SHAPE;
+  if (n % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!scale || !workspace) return MOE_ERR_NULL;
+  if (n > 0 && (!x || !codes)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
+  if (workspace_bytes < moe_act_quant_workspace_bytes()) return MOE_ERR_WORKSPACE;
+  uint32_t* amax = static_cast<uint32_t*>(workspace);
+  const int cus = num_cus();
+  hipError_t e = launch_zero_words(amax, 1, stream);
+  if (e == hipSuccess && n > 0) e = launch_amax_bf16(x, n, amax, cus, stream);
+  if (e == hipSuccess) e = launch_quant_bf16(x, n, amax, codes, scale, cus, stream);
+  return hip_status(e);
+}
+
+int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
+                          moe_wdtype wdtype) {
+  (void)H; (void)I; (void)E; (void)K; (void)wdtype;
+  // One block per active expert whenever an expert can hold all its tokens:
+  // an expert receives at most T pairs, so BM >= T streams each expert's
+  // weights once.  The swapped kernels take up to 64 tokens per block.
+  if (T <= 16) return 16;
+  if (T <= 32) return 32;
+  return 64;
+}
+
+size_t moe_fused_workspace_bytes(const moe_fused_args* a) {
+  if (!a) return 0;
+  if (check_shape(a->T, a->H, a->I, a->E, a->K) != MOE_OK) return 0;
+  if (a->wdtype != MOE_BF16 && a->wdtype != MOE_FP8_E4M3) return 0;
+  return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype).total;
+}
+
+moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
+  if (!a) return MOE_ERR_NULL;
+  moe_status st = check_shape(a->T, a->H, a->I, a->E, a->K);
+  if (st != MOE_OK) return st;
+  if (a->wdtype != MOE_BF16 && a->wdtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (a->T == 0) return MOE_OK;
+  const bool fp8 = a->wdtype == MOE_FP8_E4M3;
+  if (!a->x || !a->router_logits || !a->w13 || !a->w2 || !a->out || !a->workspace)
+    return MOE_ERR_NULL;
+  if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_NULL;
+  if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->out) ||
+      !aligned16(a->workspace))
+    return MOE_ERR_UNSUPPORTED;
+  const int64_t T = a->T;
+  const int H = a->H, I = a->I, E = a->E, K = a->K;
+  const FusedLayout L = fused_layout(T, H, I, E, K, a->wdtype);
+  if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  int32_t* ids = a->topk_ids_out ? a->topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* wts = a->topk_weights_out ? a->topk_weights_out : reinterpret_cast<float*>(ws + L.wts);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + L.bexp);
+  int32_t* npp = reinterpret_cast<int32_t*>(ws + L.npp);
+  int32_t* rank = reinterpret_cast<int32_t*>(ws + L.rank);
+  uint32_t* amax_x = reinterpret_cast<uint32_t*>(ws + L.scal);
+  uint32_t* amax_a = amax_x + 1;
+  uint8_t* qx = ws + L.qx;
+  void* abuf = ws + L.a;
+  uint8_t* qa = ws + L.qa;
+  float* dw = reinterpret_cast<float*>(ws + L.dw);
+  const int P = (int)(T * K);
+  const int cus = num_cus();
+  const int welem = fp8 ? 1 : 2;
+
+  // a1 (also clears the two amax words for this call)
+  hipError_t e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x, 2,
+                               stream);
+  // a0
+  if (e == hipSuccess && fp8) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
+  if (e == hipSuccess && fp8) e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
+  // a2
+  if (e == hipSuccess) e = launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
+
+  // a3 + a4
+  GemmParams g{};
+  g.sorted_ids = sorted;
+  g.block_expert = bexp;
+  g.num_post_pad = npp;
+  g.BM = L.bm;
+  g.P = P;
+  g.I = I;
+  g.H = H;
+  if (e == hipSuccess) {
+    g.W = static_cast<const uint8_t*>(a->w13);
+    g.w_expert_bytes = (int64_t)2 * I * H * welem;
+    g.row_bytes = (int64_t)H * welem;
+    g.B = fp8 ? qx : static_cast<const uint8_t*>(a->x);
+    g.b_row_div = K;
+    g.tiles = (I + 63) / 64;
+    g.w_scale = fp8 ? a->w13_scale : nullptr;
+    g.act_amax = fp8 ? amax_x : nullptr;
+    g.a_out = abuf;
+    g.a_amax = fp8 ? amax_a : nullptr;
+    e = launch_gemm_swapab(kGateUp, fp8, g, (int)(L.nblk * g.tiles), cus, stream);
+  }
+  // intermediate quantisation (FP8)
+  if (e == hipSuccess && fp8)
+    e = launch_quant_f32(static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus, stream);
+  // a5
+  if (e == hipSuccess) {
+    const int rows = swapab_down_rows_per_item();
+    g.W = static_cast<const uint8_t*>(a->w2);
+    g.w_expert_bytes = (int64_t)H * I * welem;
+    g.row_bytes = (int64_t)I * welem;
+    g.B = fp8 ? qa : static_cast<const uint8_t*>(abuf);
+    g.b_row_div = 1;
+    g.tiles = (H + rows - 1) / rows;
+    g.w_scale = fp8 ? a->w2_scale : nullptr;
+    g.act_amax = fp8 ? amax_a : nullptr;
+    g.dw = dw;
+    g.topk_w = wts;
+    e = launch_gemm_swapab(kDown, fp8, g, (int)(L.nblk * g.tiles), cus, stream);
+  }
+  // a6
+  if (e == hipSuccess) e = launch_combine(dw, T, K, H, a->out, cus, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

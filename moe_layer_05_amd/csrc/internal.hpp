@@ -1,0 +1,63 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGateUp = 0;
+constexpr int kDown = 1;
+constexpr int kDownRA = 2;     // 16-row tiles per wave in the down projection
+
+// Arguments of the grouped expert GEMMs (gate/up and down).
+struct GemmParams {
+  const uint8_t* W;            // expert weights [E][R][L] (bytes)
+  int64_t w_expert_bytes;      // bytes of one expert's matrix
+  int64_t row_bytes;           // bytes of one row of W and of B (L * elem)
+  const uint8_t* B;            // activation rows (x / codes of x / a / codes of a)
+  int b_row_div;               // B row of a pair: pair / b_row_div
+  const int32_t* sorted_ids;   // aligned layout
+  const int32_t* block_expert;
+  const int32_t* num_post_pad;
+  int BM;                      // tokens per block
+  int P;                       // pairs (= sentinel)
+  int tiles;                   // work items per block
+  const float* w_scale;        // [E] (FP8) or nullptr
+  const uint32_t* act_amax;    // amax bits of B's quantisation (FP8) or nullptr
+  // gate/up
+  void* a_out;                 // [P][I] float32 (FP8 path) or bfloat16
+  uint32_t* a_amax;            // amax bits of a (FP8) or nullptr
+  int I;
+  // down
+  float* dw;                   // [P][H] weighted expert outputs
+  const float* topk_w;         // [P] routing weights
+  int H;
+};
+
+hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renorm,
+                         int32_t* ids, float* wts, uint32_t* zero_words, int n_zero,
+                         hipStream_t stream);
+
+size_t align_lds_bytes(int E);
+hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
+                        hipStream_t stream);
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream);
+hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
+                            hipStream_t stream);
+hipError_t launch_quant_bf16(const void* x, int64_t n, const uint32_t* amax, uint8_t* codes,
+                             float* scale_out, int num_cus, hipStream_t stream);
+hipError_t launch_quant_f32(const float* a, int64_t n, const uint32_t* amax, uint8_t* codes,
+                            int num_cus, hipStream_t stream);
+
+int swapab_down_rows_per_item();
+hipError_t launch_gemm_swapab(int mode, bool fp8, const GemmParams& p, int max_items,
+                              int num_cus, hipStream_t stream);
+
+hipError_t launch_combine(const float* dw, int64_t T, int K, int H, void* out, int num_cus,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,114 @@
+// a0 and the intermediate quantisation of a4: per-tensor E4M3.
+//
+// FP8 E4M3 (4 exponent, 3 mantissa bits) with one scale per tensor:
+// kongchang.com page, FP8 explainer under "Triton Backend Routing"; aib.vote
+// page, third paragraph ("tensor-quantized" FP8 MoE).
+//
+// Two grid-wide steps: an amax reduction (wave max, one atomicMax of the
+// float bits per wave) and the quantisation, which reads the finished amax,
+// forms s = amax / 448 and writes E4M3(v / s) with an IEEE division, so the
+// codes are exactly those of a float32 reference.  Both kernels stream with
+// 16-byte loads and are bandwidth-bound.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+// amax over n bfloat16 values (n % 8 == 0), 8 per thread per step.
+__global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict__ x, int64_t n8,
+                                                        uint32_t* __restrict__ amax) {
+  float m = 0.0f;
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n8;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    uint4 q = x[j];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(q.x)), fabsf(bf16_hi(q.x))),
+                       fmaxf(fabsf(bf16_lo(q.y)), fabsf(bf16_hi(q.y)))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(q.z)), fabsf(bf16_hi(q.z))),
+                       fmaxf(fabsf(bf16_lo(q.w)), fabsf(bf16_hi(q.w)))));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & (kWave - 1)) == 0 && m > 0.0f) atomic_max_nonneg(amax, m);
+}
+
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d, float s) {
+  return f32_to_e4m3(a / s) | (f32_to_e4m3(b / s) << 8) | (f32_to_e4m3(c / s) << 16) |
+         (f32_to_e4m3(d / s) << 24);
+}
+
+// codes = E4M3(x / s), 8 bfloat16 in -> 8 codes out per thread per step.
+__global__ __launch_bounds__(256) void quant_bf16_kernel(const uint4* __restrict__ x, int64_t n8,
+                                                         const uint32_t* __restrict__ amax,
+                                                         uint2* __restrict__ codes,
+                                                         float* __restrict__ scale_out) {
+  const float s = scale_from_amax_bits(*amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n8;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    uint4 q = x[j];
+    uint2 o;
+    o.x = pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
+    o.y = pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
+    codes[j] = o;
+  }
+}
+
+// codes = E4M3(a / s) for float32 a (n % 8 == 0), the amax came from the
+// producer of a.
+__global__ __launch_bounds__(256) void quant_f32_kernel(const float4* __restrict__ a, int64_t n8,
+                                                        const uint32_t* __restrict__ amax,
+                                                        uint2* __restrict__ codes) {
+  const float s = scale_from_amax_bits(*amax);
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n8;
+       j += (int64_t)gridDim.x * blockDim.x) {
+    float4 p = a[2 * j], q = a[2 * j + 1];
+    uint2 o;
+    o.x = pack4(p.x, p.y, p.z, p.w, s);
+    o.y = pack4(q.x, q.y, q.z, q.w, s);
+    codes[j] = o;
+  }
+}
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+unsigned stream_grid(int64_t n8, int num_cus) {
+  int64_t blocks = (n8 + 255) / 256;
+  int64_t cap = (int64_t)num_cus * 8;
+  if (blocks > cap) blocks = cap;
+  return (unsigned)(blocks > 0 ? blocks : 1);
+}
+
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream) {
+  zero_words_kernel<<<1, 64, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
+                            hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  amax_bf16_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
+      static_cast<const uint4*>(x), n8, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_bf16(const void* x, int64_t n, const uint32_t* amax, uint8_t* codes,
+                             float* scale_out, int num_cus, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  quant_bf16_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
+      static_cast<const uint4*>(x), n8, amax, reinterpret_cast<uint2*>(codes), scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_f32(const float* a, int64_t n, const uint32_t* amax, uint8_t* codes,
+                            int num_cus, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  quant_f32_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
+      reinterpret_cast<const float4*>(a), n8, amax, reinterpret_cast<uint2*>(codes));
+  return hipGetLastError();
+}
+
+}  // namespace moe
