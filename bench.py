@@ -1,0 +1,336 @@
+"""Throughput of the fused MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--T T]
+
+A step is one ``moe_fused_forward`` over one batch of T tokens: router, sort
+by expert, gate/up product with SiLU-and-mul, down product, weighted combine
+(and both E4M3 quantisations when the experts are FP8).  Inputs are seeded,
+synthetic and resident in HBM before the timed region.  The default workload
+is the bfloat16 decode layer H=4096, I=14336, E=8, K=2 at T=64 tokens.
+
+Printed: ONE JSON line with tokens/s, the whole-layer algorithmic HBM rate,
+the roofline of the dominant kernel (timed with the library's stage events on
+the stream the kernels run on), per-stage times, a parity check of the same
+code on a sub-batch against the CPU oracle, and the oracle's own rate on that
+sub-batch (``cpu_baseline``).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0                          # MI355X HBM3E
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense MFMA
+METRIC = "MoE-layer tokens/s + HBM GB/s % peak (decode T=1..64); fp8 TFLOP/s (T=4096)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bf16_decode")
+    ap.add_argument("--T", type=int, default=None,
+                    help="tokens per batch (default: the largest decode batch, "
+                         "or 4096 for the prefill workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle work the cpu_baseline sample aims at")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="before the layer, copy this many MiB once with a plain "
+                         "device copy (a known-size reference for HBM counters)")
+    return ap.parse_args()
+
+
+def source_digest():
+    """sha256 of the HIP sources; traffic counters are valid for one digest."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "moe_layer_05_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, T, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter runs, or
+    None when there are none for this workload or the kernels have changed."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            db = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = db.get(f"{workload}/T{T}")
+    if not rec or rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Work:
+    """Sizes and algorithmic work of one call, from the actual routing."""
+
+    def __init__(self, cfg, T, ids):
+        import numpy as np
+        self.cfg, self.T = cfg, T
+        fp8 = cfg.wdtype == "fp8"
+        bw = 1 if fp8 else 2
+        H, I, E, K = cfg.H, cfg.I, cfg.E, cfg.K
+        P = T * K
+        self.active = int(np.unique(ids).size)
+        w13_e, w2_e = 2 * I * H * bw, H * I * bw
+        sc = 8 if fp8 else 0
+        # whole layer: active experts' weights (+ scales), x, logits, out
+        self.layer_bytes = self.active * (w13_e + w2_e + sc) + T * H * 2 + T * E * 4 + T * H * 2
+        self.layer_flops = 6.0 * H * I * P
+        # gate/up kernel: its experts' w13, the x rows (E4M3 codes or bf16)
+        # and the intermediate it writes (float32 for the FP8 path, bf16 else)
+        self.stage_bytes = {
+            "gate_up": self.active * (w13_e + sc // 2) + T * H * (1 if fp8 else 2)
+                       + P * I * (4 if fp8 else 2),
+            "down": self.active * (w2_e + sc // 2) + P * I * (1 if fp8 else 2) + P * H * 4 + P * 4,
+        }
+        self.stage_flops = {"gate_up": 4.0 * H * I * P, "down": 2.0 * H * I * P}
+        self.kind = "fp8" if fp8 else "bf16"
+
+
+def roofline(work, stage, us):
+    """Roofline entry of one kernel: whichever of HBM and MFMA bounds it."""
+    b = work.stage_bytes[stage]
+    f = work.stage_flops[stage]
+    peak_f = PEAK_TFLOPS[work.kind]
+    t_hbm = b / (PEAK_HBM_GBPS * 1e9)
+    t_mfma = f / (peak_f * 1e12)
+    s = us * 1e-6
+    if t_mfma > t_hbm:
+        ach = f / s / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_f, "unit": "TFLOP/s",
+                "frac": round(ach / peak_f, 4)}
+    ach = b / s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBPS, 4)}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def host_weights(w):
+    """Indexable per-expert host copies for the oracle (one expert at a time)."""
+    import torch
+
+    class Experts:
+        def __init__(self, t):
+            self.t = t
+
+        def __getitem__(self, e):
+            x = self.t[int(e)].to("cpu")
+            return x.numpy() if x.dtype == torch.uint8 else x.float().numpy()
+
+    return Experts(w)
+
+
+def oracle_and_parity(cfg, m, w, tk, budget):
+    """Time the CPU oracle on sub-batches of the first n tokens (n doubling
+    while the last run stays well inside ``budget`` seconds), and compare the
+    library on the same sub-batch.  Returns (cpu_baseline, parity)."""
+    import numpy as np
+    import torch
+    from oracle import moe as omoe
+
+    fp8 = cfg.wdtype == "fp8"
+    T = tk["x"].shape[0]
+    kw = dict(w13=host_weights(w["w13"]), w2=host_weights(w["w2"]),
+              wdtype="fp8" if fp8 else "float")
+    if fp8:
+        kw["w13_scale"] = w["w13_scale"].cpu().numpy()
+        kw["w2_scale"] = w["w2_scale"].cpu().numpy()
+    n, last = 1, None
+    while True:
+        x = tk["x"][:n].contiguous()
+        lg = tk["logits"][:n].contiguous()
+        xh = x.float().cpu().numpy()
+        lh = lg.cpu().numpy()
+        t0 = time.perf_counter()
+        ref, parts = omoe.moe_forward(xh, lh, K=cfg.K, return_parts=True, **kw)
+        dt = time.perf_counter() - t0
+        last = (n, dt, ref, parts, x, lg)
+        log(f"oracle sub-batch of {n} tokens: {dt:.2f} s")
+        if n >= T or dt * 2.3 > budget:
+            break
+        n = min(T, 2 * n)
+    n, dt, ref, parts, x, lg = last
+    out, ids, _ = m(x, lg, return_topk=True)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    err = float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+    ids_ok = bool(np.array_equal(ids.cpu().numpy(), parts["ids"]))
+    cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": blas_threads(),
+           "kind": "oracle",
+           "sample": f"first {n} of the {T} tokens run as their own batch through the "
+                     f"float64 numpy oracle (same weights), {dt:.2f} s"}
+    parity = {"tokens": n, "ids_bit_exact": ids_ok, "max_rel_err": err, "tol": 1e-2,
+              "ok": ids_ok and err <= 1e-2}
+    return cpu, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_layer_05_amd as mm
+    from moe_layer_05_amd import binding, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mm.lib()                                  # fail loudly if the library is missing
+
+    cfg = workloads.CONFIGS[args.workload]
+    T = args.T or (4096 if args.workload == "fp8_prefill_zipf" else max(cfg.Ts))
+    log(f"workload {cfg.name} T={T} H={cfg.H} I={cfg.I} E={cfg.E} K={cfg.K} {cfg.wdtype}")
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy calibration: {args.copy_calib_mib} MiB read + written once")
+
+    wdtype = "bf16" if cfg.wdtype == "float32" else cfg.wdtype
+    w = workloads.make_weights(cfg, seed=0, device=dev, wdtype=wdtype)
+    tk = workloads.make_tokens(cfg, T, seed=0, device=dev)
+    wbytes = w["w13"].numel() * w["w13"].element_size() + w["w2"].numel() * w["w2"].element_size()
+    # Rotate weight copies when one set could stay in the 256 MB last-level
+    # cache between steps, so every step streams its experts from HBM.
+    copies = 1 if wbytes >= (1 << 30) else min(8, math.ceil((2 << 30) / wbytes))
+    sets = [w] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
+                  for _ in range(copies - 1)]
+    mods = [mm.FusedMoE(s["w13"], s["w2"], cfg.K, s.get("w13_scale"), s.get("w2_scale"))
+            for s in sets]
+    x, lg = tk["x"], tk["logits"]
+    out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device=dev)
+    _, ids, _ = mods[0](x, lg, out=out, return_topk=True)
+    torch.cuda.synchronize()
+    work = Work(cfg, T, ids.cpu().numpy())
+
+    nst = len(binding.STAGES)
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        mods[i % copies](x, lg, out=out)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; in each, the library records two events around
+    # the gate/up kernel (the dominant one: two thirds of the weight bytes and
+    # of the flops) on the stream that kernel runs on.
+    G0, G1 = binding.STAGES.index("gate_up"), binding.STAGES.index("gate_up") + 1
+    evs = []
+    for _ in range(args.steps):
+        row = [None] * (nst + 1)
+        row[G0] = torch.cuda.Event(enable_timing=True)
+        row[G1] = torch.cuda.Event(enable_timing=True)
+        row[G0].record(stream)                # creates the events before the timed region
+        row[G1].record(stream)
+        evs.append(row)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        mods[i % copies](x, lg, out=out, events=evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dom = "gate_up"
+    dom_us = float(np.mean([evs[i][G0].elapsed_time(evs[i][G1]) * 1e3
+                            for i in range(args.steps)]))
+
+    # After the timed region: a breakdown with every stage boundary recorded
+    # (each record adds a few microseconds, so these steps are not the rate).
+    nb = min(args.steps, 50)
+    bevs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(nb)]
+    for row in bevs:
+        for ev in row:
+            ev.record(stream)
+    torch.cuda.synchronize()
+    for i in range(nb):
+        mods[i % copies](x, lg, out=out, events=bevs[i])
+    torch.cuda.synchronize()
+    stage_us = {}
+    for s, name in enumerate(binding.STAGES):
+        d = [bevs[i][s].elapsed_time(bevs[i][s + 1]) * 1e3 for i in range(nb)]
+        stage_us[name] = round(float(np.mean(d)), 2)
+    step_us = [bevs[i][0].elapsed_time(bevs[i][nst]) * 1e3 for i in range(nb)]
+
+    ms = elapsed / args.steps * 1e3
+    roof = roofline(work, dom, dom_us)
+    roof["kernel"] = dom
+    roof["kernel_us"] = round(dom_us, 2)
+    roof["traffic"] = load_traffic(cfg.name, T, dom)
+    roof["algorithmic_bytes"] = work.stage_bytes[dom]
+    roof["algorithmic_flops"] = work.stage_flops[dom]
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = oracle_and_parity(cfg, mods[0], w, tk, args.cpu_budget)
+
+    gbps = work.layer_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if cfg.wdtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "K": cfg.K, "weights": wdtype, "routing": cfg.routing,
+                   "active_experts": work.active, "weight_copies": copies},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layer": {"algorithmic_bytes": work.layer_bytes, "hbm_gbps": round(gbps, 1),
+                  "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+                  "tflops": round(work.layer_flops / (ms * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(work.layer_flops / (ms * 1e-3) / 1e12
+                                     / PEAK_TFLOPS[work.kind], 4),
+                  "step_us_with_all_stage_events_p50": round(float(np.percentile(step_us, 50)), 2),
+                  "step_us_with_all_stage_events_p95": round(float(np.percentile(step_us, 95)), 2)},
+        "stages_us": stage_us,
+        "parity": parity,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -182,6 +182,37 @@ int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
 
 moe_status moe_fused_forward(const moe_fused_args* args, hipStream_t stream);
 
+/*
+ * Stage boundaries of the fused forward, for timing its kernels on the
+ * stream they run on.  events[s] is recorded right before stage s is
+ * enqueued and events[MOE_STAGE_COUNT] after the last one; a stage that has
+ * no work for the weight type (the two quantisations with bfloat16 weights)
+ * has its two events back to back.
+ */
+typedef enum {
+  MOE_STAGE_ROUTE = 0,        /* a1 router                                   */
+  MOE_STAGE_ACT_QUANT = 1,    /* a0 E4M3 quantisation of x (FP8 only)        */
+  MOE_STAGE_ALIGN = 2,        /* a2 sort of the pairs by expert              */
+  MOE_STAGE_GATE_UP = 3,      /* a3+a4 gate/up product, SiLU-and-mul         */
+  MOE_STAGE_INTER_QUANT = 4,  /* E4M3 quantisation of the intermediate (FP8) */
+  MOE_STAGE_DOWN = 5,         /* a5 down product, scales, routing weight     */
+  MOE_STAGE_COMBINE = 6,      /* a6 sum over the K choices, bfloat16 output  */
+  MOE_STAGE_COUNT = 7
+} moe_stage;
+
+/*
+ * moe_fused_forward with stage events: identical work and results, plus
+ * hipEventRecord(events[s], stream) at each stage boundary.
+ *   events  [MOE_STAGE_COUNT + 1] events created by the caller (owned by the
+ *           caller; must be valid for the stream's device).  A NULL entry
+ *           skips that boundary (each record costs a few microseconds of
+ *           stream time, so a caller timing one kernel sets only its two).
+ *           A NULL array gives MOE_ERR_NULL.  A failed record gives
+ *           MOE_ERR_HIP.
+ */
+moe_status moe_fused_forward_timed(const moe_fused_args* args, hipStream_t stream,
+                                   hipEvent_t* events);
+
 #ifdef __cplusplus
 }
 #endif

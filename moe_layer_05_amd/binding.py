@@ -72,7 +72,12 @@ _SIGS = {
     "moe_fused_block_m": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int]),
     "moe_fused_forward": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p]),
+    "moe_fused_forward_timed": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p,
+                                               ctypes.c_void_p]),
 }
+
+# Stage boundaries of moe_fused_forward_timed (moe_stage in include/moe.h).
+STAGES = ("route", "act_quant", "align", "gate_up", "inter_quant", "down", "combine")
 
 
 def lib():
@@ -234,7 +239,13 @@ class FusedMoE:
             self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
         return self._ws
 
-    def __call__(self, x, logits, out=None, return_topk=False, stream=None):
+    def __call__(self, x, logits, out=None, return_topk=False, stream=None, events=None):
+        """out [T, H] bfloat16 of x [T, H] bfloat16 and logits [T, E] float32.
+
+        ``events``: optional list of len(STAGES) + 1 entries, each a
+        torch.cuda.Event created with enable_timing=True or None; the library
+        records the events at the stage boundaries on the stream
+        (moe_fused_forward_timed) and skips the None entries."""
         T = x.shape[0]
         if out is None:
             out = torch.empty(T, self.H, dtype=torch.bfloat16, device=x.device)
@@ -246,7 +257,19 @@ class FusedMoE:
         a = self.args(x, logits, out, ids, wts)
         a.workspace = ws.data_ptr()
         a.workspace_bytes = ws.numel()
-        _check(lib().moe_fused_forward(ctypes.byref(a), _stream(stream)), "moe_fused_forward")
+        if events is None:
+            _check(lib().moe_fused_forward(ctypes.byref(a), _stream(stream)), "moe_fused_forward")
+        else:
+            if len(events) != len(STAGES) + 1:
+                raise ValueError(f"need {len(STAGES) + 1} events")
+            st = stream if stream is not None else torch.cuda.current_stream()
+            for ev in events:
+                if ev is not None and ev.cuda_event == 0:
+                    ev.record(st)           # torch creates the event on its first record
+            arr = (ctypes.c_void_p * len(events))(
+                *[ev.cuda_event if ev is not None else None for ev in events])
+            _check(lib().moe_fused_forward_timed(ctypes.byref(a), _stream(stream), arr),
+                   "moe_fused_forward_timed")
         return (out, ids, wts) if return_topk else out
 
 

@@ -175,7 +175,16 @@ size_t moe_fused_workspace_bytes(const moe_fused_args* a) {
   return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype).total;
 }
 
-moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Records events[s] on the stream when the array and its entry s are set.
+hipError_t mark(hipEvent_t* events, int s, hipStream_t stream) {
+  return (events && events[s]) ? hipEventRecord(events[s], stream) : hipSuccess;
+}
+
+moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEvent_t* ev) {
   if (!a) return MOE_ERR_NULL;
   moe_status st = check_shape(a->T, a->H, a->I, a->E, a->K);
   if (st != MOE_OK) return st;
@@ -211,12 +220,16 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   const int welem = fp8 ? 1 : 2;
 
   // a1 (also clears the two amax words for this call)
-  hipError_t e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x, 2,
+  hipError_t e = mark(ev, MOE_STAGE_ROUTE, stream);
+  if (e == hipSuccess)
+    e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x, 2,
                                stream);
   // a0
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
   if (e == hipSuccess && fp8) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
   if (e == hipSuccess && fp8) e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
   // a2
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
   if (e == hipSuccess) e = launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
 
   // a3 + a4
@@ -228,6 +241,7 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
   g.P = P;
   g.I = I;
   g.H = H;
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_GATE_UP, stream);
   if (e == hipSuccess) {
     g.W = static_cast<const uint8_t*>(a->w13);
     g.w_expert_bytes = (int64_t)2 * I * H * welem;
@@ -242,9 +256,11 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
     e = launch_gemm_swapab(kGateUp, fp8, g, (int)(L.nblk * g.tiles), cus, stream);
   }
   // intermediate quantisation (FP8)
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_INTER_QUANT, stream);
   if (e == hipSuccess && fp8)
     e = launch_quant_f32(static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus, stream);
   // a5
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);
   if (e == hipSuccess) {
     const int rows = swapab_down_rows_per_item();
     g.W = static_cast<const uint8_t*>(a->w2);
@@ -260,8 +276,24 @@ moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
     e = launch_gemm_swapab(kDown, fp8, g, (int)(L.nblk * g.tiles), cus, stream);
   }
   // a6
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, stream);
   if (e == hipSuccess) e = launch_combine(dw, T, K, H, a->out, cus, stream);
+  if (e == hipSuccess) e = mark(ev, MOE_STAGE_COUNT, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_fused_forward(const moe_fused_args* a, hipStream_t stream) {
+  return fused_forward_impl(a, stream, nullptr);
+}
+
+moe_status moe_fused_forward_timed(const moe_fused_args* a, hipStream_t stream,
+                                   hipEvent_t* events) {
+  if (!events) return MOE_ERR_NULL;
+  return fused_forward_impl(a, stream, events);
 }
 
 }  // extern "C"
