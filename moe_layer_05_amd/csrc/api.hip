@@ -48,15 +48,19 @@ struct FusedLayout {
   size_t ids, wts, sorted, bexp, npp, rank, scal, qx, a, qa, dw, total;
   int bm;
   int64_t cap, nblk;
+  DecodeShape gu, dn;
 };
 
 FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   FusedLayout L{};
   const int64_t P = T * K;
   const bool fp8 = wd == MOE_FP8_E4M3;
+  const int welem = fp8 ? 1 : 2;
   L.bm = moe_fused_block_m(T, H, I, E, K, wd);
   L.nblk = max_blocks(P, E, L.bm);
   L.cap = L.nblk * L.bm;
+  L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem);
+  L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   L.ids = take(P * 4);
@@ -69,7 +73,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.qx = take(fp8 ? (size_t)T * H : 0);
   L.a = take((size_t)P * I * (fp8 ? 4 : 2));
   L.qa = take(fp8 ? (size_t)P * I : 0);
-  L.dw = take((size_t)P * H * 4);
+  L.dw = take((size_t)L.dn.splits * P * H * 4);
   L.total = off;
   return L;
 }
@@ -159,12 +163,15 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* sc
 
 int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                           moe_wdtype wdtype) {
-  (void)H; (void)I; (void)E; (void)K; (void)wdtype;
-  // One block per active expert whenever an expert can hold all its tokens:
-  // an expert receives at most T pairs, so BM >= T streams each expert's
-  // weights once.  The swapped kernels take up to 64 tokens per block.
+  (void)H; (void)I; (void)wdtype;
+  // One block per active expert whenever an expert can hold all its tokens,
+  // so each expert's weights stream from HBM once.  An expert receives at
+  // most T pairs; with many experts it receives about T*K/E, so the block is
+  // sized for a few times that mean (blocks up to 64 tokens).
   if (T <= 16) return 16;
-  if (T <= 32) return 32;
+  const int64_t mean = (E > 0) ? (T * (int64_t)K + E - 1) / E : T;
+  if (mean <= 4) return 16;
+  if (T <= 32 || mean <= 16) return 32;
   return 64;
 }
 
@@ -248,12 +255,13 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.row_bytes = (int64_t)H * welem;
     g.B = fp8 ? qx : static_cast<const uint8_t*>(a->x);
     g.b_row_div = K;
-    g.tiles = (I + 63) / 64;
+    g.groups = L.gu.groups;
+    g.splits = L.gu.splits;
     g.w_scale = fp8 ? a->w13_scale : nullptr;
     g.act_amax = fp8 ? amax_x : nullptr;
     g.a_out = abuf;
     g.a_amax = fp8 ? amax_a : nullptr;
-    e = launch_gemm_swapab(kGateUp, fp8, g, (int)(L.nblk * g.tiles), cus, stream);
+    e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, stream);
   }
   // intermediate quantisation (FP8)
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_INTER_QUANT, stream);
@@ -262,22 +270,23 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   // a5
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);
   if (e == hipSuccess) {
-    const int rows = swapab_down_rows_per_item();
     g.W = static_cast<const uint8_t*>(a->w2);
     g.w_expert_bytes = (int64_t)H * I * welem;
     g.row_bytes = (int64_t)I * welem;
     g.B = fp8 ? qa : static_cast<const uint8_t*>(abuf);
     g.b_row_div = 1;
-    g.tiles = (H + rows - 1) / rows;
+    g.groups = L.dn.groups;
+    g.splits = L.dn.splits;
     g.w_scale = fp8 ? a->w2_scale : nullptr;
     g.act_amax = fp8 ? amax_a : nullptr;
     g.dw = dw;
+    g.dw_split_stride = (int64_t)P * H;
     g.topk_w = wts;
-    e = launch_gemm_swapab(kDown, fp8, g, (int)(L.nblk * g.tiles), cus, stream);
+    e = launch_gemm_decode(kDown, fp8, g, L.dn.ra, L.nblk, stream);
   }
   // a6
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, stream);
-  if (e == hipSuccess) e = launch_combine(dw, T, K, H, a->out, cus, stream);
+  if (e == hipSuccess) e = launch_combine(dw, L.dn.splits, T, K, H, a->out, cus, stream);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COUNT, stream);
   return hip_status(e);
 }

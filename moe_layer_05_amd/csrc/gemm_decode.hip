@@ -1,0 +1,425 @@
+// a3-a6 for thin token blocks: grouped expert GEMMs with the expert weight rows
+// on the MFMA row side (the Swap-AB idea), fused epilogues, and a weight
+// stream shaped for HBM3E.
+//
+// Thin decode batches leave a matrix unit's row side mostly empty if tokens
+// take it; transposing the product, C^T = W X^T, puts the large expert
+// dimension there instead and costs nothing mathematically (toolboxkart.tech
+// page, section 1 "Swap-AB makes better use of the WGMMA tile"; kongchang.com
+// page, "Swap-AB: Making WGMMA Run at Full Utilization"; aib.vote page, second
+// paragraph: top-k=8 joins the selected experts' intermediate dimensions into
+// one large dimension).  The epilogues apply the dequantisation scales,
+// SiLU-and-mul and the routing weight in the same pass as the product
+// (aib.vote page, third paragraph).
+//
+// On gfx950 the row side of a 16x16 MFMA is 16 weight rows; tokens take the 16
+// columns.  Both operands are K-contiguous rows (W[row][k], X[token][k]):
+// lane l holds row (l % 16) and a 64-byte run of k chosen by (l / 16) in each
+// 256-byte chunk.  The MFMA pairs A and B elements by the same (lane group,
+// byte) position, so any fixed assignment of k to those positions gives the
+// full dot product; every lane therefore loads 4 x 16 contiguous bytes per row
+// per chunk with no shuffles.
+//
+// Decode is a weight stream: every byte of an active expert is read once and
+// used by at most a few tokens.  The kernel is shaped for that:
+//  - weight loads are non-temporal (the data is not reused, and streaming it
+//    past the last-level cache raises the sustained read rate of HBM3E);
+//  - each wave keeps D chunks of its rows in flight in a register ring;
+//  - the unit of work is one wave: (block b, row group g, k-split s), where a
+//    row group is RA 16-row MFMA tiles; the grid is not persistent: one wave
+//    per unit of the capacity bound, so the hardware dispatcher balances the
+//    waves over the compute units, and units past the device-side block count
+//    leave at once (the host never reads the routing);
+//  - the down product may split its reduction dimension I into S parts; each
+//    part writes its own weighted partial rows and the combine adds the parts
+//    in a fixed order, so results stay deterministic.
+// Activation rows (x, x codes, a, a codes) are small and shared by all row
+// groups of an expert; they are loaded through the caches.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = 256;           // bytes of each row per pipeline step
+constexpr int kTileBytes = 16 * kChunk;   // one 16-row tile of one chunk in LDS
+constexpr int kAuxNT = 2;             // cache policy bits of a non-temporal load
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Four 16-byte LDS reads and the wait for them, in one block: the compiler
+// does not see these reads, so it adds no conservative wait on the weight
+// loads into LDS that precede them (the kernel places those waits itself).
+__device__ __forceinline__ void lds_read4(uint4 (&d)[4], uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %5\n"
+      "ds_read_b128 %2, %6\n"
+      "ds_read_b128 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(d[0]), "=v"(d[1]), "=v"(d[2]), "=v"(d[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <bool FP8>
+struct Tile {
+  // 16x16 accumulate of one 256-byte chunk: A = 16 weight rows, B = 16 tokens.
+  static __device__ __forceinline__ v4f mma(const uint4 (&a)[4], const uint4 (&b)[4], v4f acc) {
+    if constexpr (FP8) {
+      v8i a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+      v8i b0 = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+                (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+      v8i a1 = {(int)a[2].x, (int)a[2].y, (int)a[2].z, (int)a[2].w,
+                (int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
+      v8i b1 = {(int)b[2].x, (int)b[2].y, (int)b[2].z, (int)b[2].w,
+                (int)b[3].x, (int)b[3].y, (int)b[3].z, (int)b[3].w};
+      // format 0 = E4M3 for both operands; scales 2^(127-127) = 1
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, 0, 0, 0, 127, 0, 127);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, 0, 0, 0, 127, 0, 127);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v8bf av = __builtin_bit_cast(v8bf, a[j]);
+        v8bf bv = __builtin_bit_cast(v8bf, b[j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+      }
+    }
+    return acc;
+  }
+};
+
+template <int MODE, bool FP8, int NSUB, int RA, int D>
+__global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // loads per chunk, all into LDS: 4 per 16-row weight tile, 4 per 16-token tile
+  constexpr int kTiles = RA + NSUB;
+  constexpr int kLoads = 4 * kTiles;
+  static_assert((D - 1) * kLoads <= 63, "ring deeper than the vmcnt counter");
+
+  const int lane = threadIdx.x;
+  const int g4 = lane >> 4;
+  const int r16 = lane & 15;
+
+  const int64_t unit = blockIdx.x;                 // one wave per workgroup
+  const int per_block = p.groups * p.splits;
+  const int b = (int)(unit / per_block);
+  if (b >= p.num_post_pad[0] / p.BM) return;       // past the routed blocks
+  const int rem = (int)(unit - (int64_t)b * per_block);
+  const int grp = rem % p.groups;
+  const int split = rem / p.groups;
+  const int e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
+
+  const int row_bytes = (int)p.row_bytes;
+  const int nchunks = (row_bytes + kChunk - 1) / kChunk;
+  const int nfull = row_bytes / kChunk;
+  const int cps = (nchunks + p.splits - 1) / p.splits;
+  const int c_begin = split * cps;
+  const int c_end = min(nchunks, c_begin + cps);
+
+  // valid tokens of this block (sentinels sit at the end of a block)
+  const int32_t* blk = p.sorted_ids + (int64_t)b * p.BM;
+  const int32_t sid = (lane < p.BM) ? blk[lane] : p.P;
+  const int count = __popcll(__ballot(sid < p.P));
+  const int nsub = (count + 15) >> 4;
+
+  // ---- tiles: RA weight tiles (16 rows each) then NSUB token tiles (16
+  // activation rows each), 256 bytes of each row per chunk, HBM/L2 -> LDS.
+  // Load instruction i of a tile covers tile rows 4i + g4 with lane piece
+  // r16; LDS slot (row rr, position q) holds the row's 16-byte piece q ^ rr,
+  // so the MFMA-layout reads (16 rows, one piece) hit 16 bank groups.
+  const uint8_t* wexp = p.W + (int64_t)e * p.w_expert_bytes;
+  int row0[RA];
+  bool a_ok[RA];
+  const uint8_t* src[kTiles][4];                   // the lane's row start per load
+#pragma unroll
+  for (int ra = 0; ra < RA; ++ra) {
+    int base;
+    if constexpr (MODE == kGateUp) {
+      // pairs of tiles: gate rows c0.., up rows I + c0..
+      const int c0 = (grp * (RA / 2) + ra / 2) * 16;
+      row0[ra] = c0;
+      a_ok[ra] = c0 < p.I;
+      base = (ra & 1) ? p.I + c0 : c0;
+    } else {
+      const int r0 = (grp * RA + ra) * 16;
+      row0[ra] = r0;
+      a_ok[ra] = r0 < p.H;
+      base = r0;
+    }
+    if (!a_ok[ra]) base = 0;                       // a valid row; never stored
+#pragma unroll
+    for (int i = 0; i < 4; ++i) src[ra][i] = wexp + (int64_t)(base + 4 * i + g4) * row_bytes;
+  }
+  if (!a_ok[0]) return;                            // no tile of this wave exists
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int slot = s * 16 + 4 * i + g4;
+      const int32_t pair = slot < p.BM ? blk[slot] : p.P;
+      // padding slots read activation row 0; their columns are never stored
+      const int64_t brow = pair < p.P ? (int64_t)(pair / p.b_row_div) : 0;
+      src[RA + s][i] = p.B + brow * row_bytes;
+    }
+  uint32_t pc[4];                                  // the lane's piece offset per load
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pc[i] = (uint32_t)((r16 ^ (4 * i + g4)) * 16);
+
+  uint8_t* ring = smem;
+  uint32_t rd[4];                                  // MFMA-layout read addresses
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rd[j] = lds_addr(ring) + r16 * kChunk + (((4 * j + g4) ^ r16) * 16);
+
+  v4f acc[RA][NSUB];
+#pragma unroll
+  for (int ra = 0; ra < RA; ++ra)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[ra][s] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Every load of the loop goes to LDS and is counted by the explicit waits;
+  // the compiler sees no load whose register result it must wait for.
+  auto issue = [&](int d, int c) {
+    const uint32_t off = (uint32_t)c * kChunk;
+#pragma unroll
+    for (int t = 0; t < RA; ++t)                   // weights: read once, non-temporal
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src[t][i] + off + pc[i]),
+            (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, kAuxNT);
+#pragma unroll
+    for (int t = RA; t < kTiles; ++t)              // activations: shared, cached
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src[t][i] + off + pc[i]),
+            (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, 0);
+  };
+  // tail: pieces past the row end are read from the row start (valid memory)
+  // and zeroed on the token side after the read.
+  auto issue_tail = [&](int c) {
+    const uint32_t off = (uint32_t)c * kChunk;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool in = off + pc[i] < (uint32_t)row_bytes;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src[t][i] + (in ? off + pc[i] : 0u)),
+            (lds_void*)(ring + t * kTileBytes + i * 1024), 16, 0, 0);
+      }
+  };
+  auto consume = [&](int d, bool tail, uint32_t off) {
+    uint4 bt[NSUB][4];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const uint32_t o = (uint32_t)(d * kTiles + RA + s) * kTileBytes;
+      lds_read4(bt[s], rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
+      if (tail) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (off + (4 * j + g4) * 16 >= (uint32_t)row_bytes) bt[s][j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra) {
+      uint4 a[4];
+      const uint32_t o = (uint32_t)(d * kTiles + ra) * kTileBytes;
+      lds_read4(a, rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[ra][s] = Tile<FP8>::mma(a, bt[s], acc[ra][s]);
+    }
+  };
+
+  // Ring of D chunks over the full chunks of this part: after consuming
+  // chunk c + d the wave issues chunk c + D + d into the freed stage, so
+  // D - 1 chunks stay in flight; the last chunks drain with full waits.
+  const int c_full = min(c_end, nfull);
+  const int nc = c_full - c_begin;
+  if (nc >= D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d, c_begin + d);
+    int c = c_begin;
+    for (; c + 2 * D <= c_full; c += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        wait_vmcnt<(D - 1) * kLoads>();
+        consume(d, false, 0);
+        issue(d, c + D + d);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      wait_vmcnt<0>();
+      consume(d, false, 0);
+      if (c + D + d < c_full) issue(d, c + D + d);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c + D + d < c_full) {
+        wait_vmcnt<0>();
+        consume(d, false, 0);
+      }
+    }
+  } else if (nc > 0) {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < nc) issue(d, c_begin + d);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < nc) consume(d, false, 0);
+  }
+  // The row's partial last chunk, when this part holds it.
+  if (c_end > nfull) {
+    issue_tail(nfull);
+    wait_vmcnt<0>();
+    consume(0, true, (uint32_t)nfull * kChunk);
+  }
+
+  // ------------------------------------------------------------ epilogue
+  float scale = 1.0f;
+  if constexpr (FP8) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[e];
+
+  if constexpr (MODE == kGateUp) {
+    float local_max = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s >= nsub) continue;
+      const int32_t pair = blk[s * 16 + r16];
+      if (pair >= p.P) continue;
+#pragma unroll
+      for (int cg = 0; cg < RA / 2; ++cg) {
+        if (!a_ok[2 * cg]) continue;
+        const int col = row0[2 * cg] + 4 * g4;
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gt = acc[2 * cg][s][v] * scale;
+          const float up = acc[2 * cg + 1][s][v] * scale;
+          av[v] = gt / (1.0f + __expf(-gt)) * up;
+          local_max = fmaxf(local_max, fabsf(av[v]));
+        }
+        if constexpr (FP8) {
+          float* dst = static_cast<float*>(p.a_out) + (int64_t)pair * p.I + col;
+          *reinterpret_cast<float4*>(dst) = make_float4(av[0], av[1], av[2], av[3]);
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.a_out) + (int64_t)pair * p.I + col;
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(av[0]) | (f32_to_bf16_bits(av[1]) << 16);
+          pk.y = f32_to_bf16_bits(av[2]) | (f32_to_bf16_bits(av[3]) << 16);
+          *reinterpret_cast<uint2*>(dst) = pk;
+        }
+      }
+    }
+    if constexpr (FP8) {
+      local_max = wave_max(local_max);
+      if (lane == 0 && local_max > 0.0f) atomic_max_nonneg(p.a_amax, local_max);
+    }
+  } else {
+    float* part = p.dw + (int64_t)split * p.dw_split_stride;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      if (s >= nsub) continue;
+      const int32_t pair = blk[s * 16 + r16];
+      if (pair >= p.P) continue;
+      const float sc = scale * p.topk_w[pair];
+#pragma unroll
+      for (int ra = 0; ra < RA; ++ra) {
+        if (!a_ok[ra]) continue;
+        float* dst = part + (int64_t)pair * p.H + row0[ra] + 4 * g4;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(acc[ra][s][0] * sc, acc[ra][s][1] * sc, acc[ra][s][2] * sc,
+                        acc[ra][s][3] * sc);
+      }
+    }
+  }
+}
+
+template <int MODE, bool FP8, int NSUB, int RA, int D>
+hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
+  const int lds = D * (RA + NSUB) * kTileBytes;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D><<<grid, dim3(64), lds, stream>>>(p);
+  return hipGetLastError();
+}
+
+// Ring depth per (weight tiles, token tiles) of a wave: each wave holds
+// D * (RA + NSUB) * 4 KB of LDS, so the 160 KB of a compute unit keep about
+// 64 KB of weights in flight.
+template <int MODE, bool FP8, int RA>
+hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, hipStream_t stream) {
+  switch (nsub_max) {
+    case 1: return launch_one<MODE, FP8, 1, RA, (RA == 1 ? 5 : (RA == 2 ? 4 : 1))>(p, grid, stream);
+    case 2: return launch_one<MODE, FP8, 2, RA, (RA == 1 ? 3 : (RA == 2 ? 3 : 1))>(p, grid, stream);
+    case 4: return launch_one<MODE, FP8, 4, RA, (RA == 1 ? 2 : (RA == 2 ? 2 : 1))>(p, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int MODE, int RA>
+hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid,
+                        hipStream_t stream) {
+  return fp8 ? launch_nsub<MODE, true, RA>(p, nsub_max, grid, stream)
+             : launch_nsub<MODE, false, RA>(p, nsub_max, grid, stream);
+}
+
+}  // namespace
+
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes) {
+  DecodeShape s{};
+  const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
+  if (mode == kGateUp) {
+    // rows = I: a wave owns 16 columns, i.e. 16 gate and 16 up rows.
+    s.ra = 2;
+    s.groups = (rows + 15) / 16;
+    s.splits = 1;
+  } else {
+    // rows = H: RA 16-row tiles per wave; short rows take more tiles.
+    s.ra = row_bytes >= 1024 ? 1 : (row_bytes >= 512 ? 2 : 4);
+    s.groups = (rows + 16 * s.ra - 1) / (16 * s.ra);
+    // Split the reduction when there are too few waves to cover the chip
+    // (about 2048 in flight), keeping >= 8 chunks per part.
+    const int64_t units = nblk_cap * s.groups;
+    int sp = 1;
+    while (units * sp < 2048 && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
+    s.splits = sp;
+  }
+  return s;
+}
+
+hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
+                              hipStream_t stream) {
+  const int nsub_max = p.BM / 16;
+  const int64_t wgs = nblk_cap * p.groups * p.splits;   // one wave each
+  if (wgs <= 0) return hipSuccess;
+  if (wgs > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
+  if (mode == kGateUp) {
+    if (ra == 2) return launch_dtype<kGateUp, 2>(fp8, p, nsub_max, grid, stream);
+    return hipErrorInvalidValue;
+  }
+  if (ra == 1) return launch_dtype<kDown, 1>(fp8, p, nsub_max, grid, stream);
+  if (ra == 2) return launch_dtype<kDown, 2>(fp8, p, nsub_max, grid, stream);
+  if (ra == 4) return launch_dtype<kDown, 4>(fp8, p, nsub_max, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

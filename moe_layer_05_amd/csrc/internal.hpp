@@ -9,7 +9,6 @@ namespace moe {
 
 constexpr int kGateUp = 0;
 constexpr int kDown = 1;
-constexpr int kDownRA = 2;     // 16-row tiles per wave in the down projection
 
 // Arguments of the grouped expert GEMMs (gate/up and down).
 struct GemmParams {
@@ -23,7 +22,8 @@ struct GemmParams {
   const int32_t* num_post_pad;
   int BM;                      // tokens per block
   int P;                       // pairs (= sentinel)
-  int tiles;                   // work items per block
+  int groups;                  // row groups per block (one wave each)
+  int splits;                  // parts of the reduction dimension
   const float* w_scale;        // [E] (FP8) or nullptr
   const uint32_t* act_amax;    // amax bits of B's quantisation (FP8) or nullptr
   // gate/up
@@ -31,9 +31,16 @@ struct GemmParams {
   uint32_t* a_amax;            // amax bits of a (FP8) or nullptr
   int I;
   // down
-  float* dw;                   // [P][H] weighted expert outputs
+  float* dw;                   // [splits][P][H] weighted expert outputs
+  int64_t dw_split_stride;     // elements between parts (P * H)
   const float* topk_w;         // [P] routing weights
   int H;
+};
+
+// Work decomposition of a decode GEMM launch (chosen on the host from the
+// shape only): RA 16-row tiles per wave, row groups per block, k-splits.
+struct DecodeShape {
+  int ra, groups, splits;
 };
 
 hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renorm,
@@ -53,11 +60,11 @@ hipError_t launch_quant_bf16(const void* x, int64_t n, const uint32_t* amax, uin
 hipError_t launch_quant_f32(const float* a, int64_t n, const uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream);
 
-int swapab_down_rows_per_item();
-hipError_t launch_gemm_swapab(int mode, bool fp8, const GemmParams& p, int max_items,
-                              int num_cus, hipStream_t stream);
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes);
+hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
+                              hipStream_t stream);
 
-hipError_t launch_combine(const float* dw, int64_t T, int K, int H, void* out, int num_cus,
-                          hipStream_t stream);
+hipError_t launch_combine(const float* dw, int splits, int64_t T, int K, int H, void* out,
+                          int num_cus, hipStream_t stream);
 
 }  // namespace moe
