@@ -145,9 +145,15 @@ def test_fused_validation(L):
 
 
 def test_fused_block_m_and_workspace(L):
+    # a block holds one expert's tokens; its size follows the expected tokens
+    # per expert (T*K/E), so an expert's weights stream once per call
     bm = [L.moe_fused_block_m(T, 7168, 2048, 256, 8, 1) for T in (1, 8, 16, 17, 32, 64, 4096)]
     assert all(b in (16, 32, 64, 128, 256) for b in bm)
-    assert bm[0] >= 1 and bm[2] >= 16 and bm[4] >= 32 and bm[5] >= 64
+    assert bm[:3] == [16, 16, 16]                    # T <= 16: one 16-token block
+    assert bm[5] == 16                               # 2 tokens per expert on average
+    assert L.moe_fused_block_m(64, 4096, 14336, 8, 2, 0) == 32     # 16 per expert
+    assert L.moe_fused_block_m(256, 4096, 192, 128, 8, 1) == 32    # 16 per expert
+    assert L.moe_fused_block_m(4096, 7168, 2048, 256, 8, 1) == 64  # 128 per expert
     a = _args()
     n1 = L.moe_fused_workspace_bytes(ctypes.byref(a))
     assert n1 > 8 * 4 * (256 * 4)                    # at least the pair outputs
