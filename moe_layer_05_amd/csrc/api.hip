@@ -3,7 +3,8 @@
 // allocated and nothing synchronises the host.
 #include <mutex>
 
-#include "../../include/moe.h"
+#include "moe.h"
+#include "device_common.hpp"
 #include "internal.hpp"
 
 namespace moe {
@@ -69,7 +70,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.bexp = take(L.nblk * 4);
   L.npp = take(4);
   L.rank = take(P * 4);
-  L.scal = take(2 * 4);
+  L.scal = take(2 * kAmaxWords * 4);     // amax blocks of x and of a
   L.qx = take(fp8 ? (size_t)T * H : 0);
   L.a = take((size_t)P * I * (fp8 ? 4 : 2));
   L.qa = take(fp8 ? (size_t)P * I : 0);
@@ -143,7 +144,7 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, i
                                  num_post_pad, static_cast<int32_t*>(workspace), stream));
 }
 
-size_t moe_act_quant_workspace_bytes(void) { return kAlignBytes; }
+size_t moe_act_quant_workspace_bytes(void) { return round_up(kAmaxWords * 4); }
 
 moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* scale,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -155,7 +156,7 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* sc
   if (workspace_bytes < moe_act_quant_workspace_bytes()) return MOE_ERR_WORKSPACE;
   uint32_t* amax = static_cast<uint32_t*>(workspace);
   const int cus = num_cus();
-  hipError_t e = launch_zero_words(amax, 1, stream);
+  hipError_t e = launch_zero_amax(amax, 1, stream);
   if (e == hipSuccess && n > 0) e = launch_amax_bf16(x, n, amax, cus, stream);
   if (e == hipSuccess) e = launch_quant_bf16(x, n, amax, codes, scale, cus, stream);
   return hip_status(e);
@@ -216,8 +217,8 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   int32_t* bexp = reinterpret_cast<int32_t*>(ws + L.bexp);
   int32_t* npp = reinterpret_cast<int32_t*>(ws + L.npp);
   int32_t* rank = reinterpret_cast<int32_t*>(ws + L.rank);
-  uint32_t* amax_x = reinterpret_cast<uint32_t*>(ws + L.scal);
-  uint32_t* amax_a = amax_x + 1;
+  uint32_t* amax_x = reinterpret_cast<uint32_t*>(ws + L.scal);   // amax blocks
+  uint32_t* amax_a = amax_x + kAmaxWords;
   uint8_t* qx = ws + L.qx;
   void* abuf = ws + L.a;
   uint8_t* qa = ws + L.qa;
@@ -226,10 +227,10 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   const int cus = num_cus();
   const int welem = fp8 ? 1 : 2;
 
-  // a1 (also clears the two amax words for this call)
+  // a1 (also clears the amax slots of x and a for this call)
   hipError_t e = mark(ev, MOE_STAGE_ROUTE, stream);
   if (e == hipSuccess)
-    e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x, 2,
+    e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x, fp8 ? 2 : 0,
                                stream);
   // a0
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
@@ -258,7 +259,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.groups = L.gu.groups;
     g.splits = L.gu.splits;
     g.w_scale = fp8 ? a->w13_scale : nullptr;
-    g.act_amax = fp8 ? amax_x : nullptr;
+    g.act_amax = fp8 ? amax_x + kAmaxFinal : nullptr;
     g.a_out = abuf;
     g.a_amax = fp8 ? amax_a : nullptr;
     e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, stream);
@@ -278,7 +279,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.groups = L.dn.groups;
     g.splits = L.dn.splits;
     g.w_scale = fp8 ? a->w2_scale : nullptr;
-    g.act_amax = fp8 ? amax_a : nullptr;
+    g.act_amax = fp8 ? amax_a + kAmaxFinal : nullptr;
     g.dw = dw;
     g.dw_split_stride = (int64_t)P * H;
     g.topk_w = wts;

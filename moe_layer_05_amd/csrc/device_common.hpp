@@ -66,9 +66,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- amax
+
+// A per-tensor amax is gathered in kAmaxSlots words, each on its own 128-byte
+// line, so thousands of waves updating it do not serialise on one address;
+// after the producer kernel has finished, one wave reads all slots.  Layout of
+// an amax block: slot i at word i * kAmaxStride, then the final value (written
+// once by the consumer) at word kAmaxFinal.
+constexpr int kAmaxSlots = 64;
+constexpr int kAmaxStride = 32;
+constexpr int kAmaxFinal = kAmaxSlots * kAmaxStride;
+constexpr int kAmaxWords = kAmaxFinal + 32;
+
 // Non-negative floats order like their bit patterns: atomicMax on the bits.
-__device__ __forceinline__ void atomic_max_nonneg(uint32_t* p, float v) {
-  atomicMax(p, __float_as_uint(v));
+__device__ __forceinline__ void amax_slot_max(uint32_t* block, uint32_t key, float v) {
+  atomicMax(block + (key % kAmaxSlots) * kAmaxStride, __float_as_uint(v));
+}
+
+// Word to clear for index t < kAmaxSlots * nblocks of consecutive amax blocks.
+__device__ __forceinline__ int amax_zero_index(int t) {
+  return (t / kAmaxSlots) * kAmaxWords + (t % kAmaxSlots) * kAmaxStride;
+}
+
+// The maximum over all slots of an amax block, in every lane of the wave.
+__device__ __forceinline__ float amax_slots_reduce(const uint32_t* block) {
+  const int lane = threadIdx.x & (kWave - 1);
+  return wave_max(__uint_as_float(block[lane * kAmaxStride]));
 }
 
 }  // namespace moe

@@ -54,6 +54,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Four 16-byte LDS reads and the wait for them, in one block: the compiler
 // does not see these reads, so it adds no conservative wait on the weight
 // loads into LDS that precede them (the kernel places those waits itself).
+// The outputs are early-clobber: a read's data may land before a later read
+// of the block has taken its address, so no output may share a register with
+// an address.
 __device__ __forceinline__ void lds_read4(uint4 (&d)[4], uint32_t a0, uint32_t a1, uint32_t a2,
                                           uint32_t a3) {
   asm volatile(
@@ -62,7 +65,7 @@ __device__ __forceinline__ void lds_read4(uint4 (&d)[4], uint32_t a0, uint32_t a
       "ds_read_b128 %2, %6\n"
       "ds_read_b128 %3, %7\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(d[0]), "=v"(d[1]), "=v"(d[2]), "=v"(d[3])
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
       : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
 }
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
     }
     if constexpr (FP8) {
       local_max = wave_max(local_max);
-      if (lane == 0 && local_max > 0.0f) atomic_max_nonneg(p.a_amax, local_max);
+      if (lane == 0 && local_max > 0.0f) amax_slot_max(p.a_amax, (uint32_t)unit, local_max);
     }
   } else {
     float* part = p.dw + (int64_t)split * p.dw_split_stride;

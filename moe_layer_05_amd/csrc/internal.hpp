@@ -25,10 +25,10 @@ struct GemmParams {
   int groups;                  // row groups per block (one wave each)
   int splits;                  // parts of the reduction dimension
   const float* w_scale;        // [E] (FP8) or nullptr
-  const uint32_t* act_amax;    // amax bits of B's quantisation (FP8) or nullptr
+  const uint32_t* act_amax;    // final amax bits of B's quantisation (FP8) or nullptr
   // gate/up
   void* a_out;                 // [P][I] float32 (FP8 path) or bfloat16
-  uint32_t* a_amax;            // amax bits of a (FP8) or nullptr
+  uint32_t* a_amax;            // amax block (slots) of a (FP8) or nullptr
   int I;
   // down
   float* dw;                   // [splits][P][H] weighted expert outputs
@@ -44,7 +44,7 @@ struct DecodeShape {
 };
 
 hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renorm,
-                         int32_t* ids, float* wts, uint32_t* zero_words, int n_zero,
+                         int32_t* ids, float* wts, uint32_t* zero_amax, int n_amax,
                          hipStream_t stream);
 
 size_t align_lds_bytes(int E);
@@ -52,12 +52,12 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream);
 
-hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream);
+hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream);
 hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
                             hipStream_t stream);
-hipError_t launch_quant_bf16(const void* x, int64_t n, const uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
                              float* scale_out, int num_cus, hipStream_t stream);
-hipError_t launch_quant_f32(const float* a, int64_t n, const uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream);
 
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes);

@@ -5,10 +5,11 @@
 // page, third paragraph ("tensor-quantized" FP8 MoE).
 //
 // Two grid-wide steps: an amax reduction (wave max, one atomicMax of the
-// float bits per wave) and the quantisation, which reads the finished amax,
-// forms s = amax / 448 and writes E4M3(v / s) with an IEEE division, so the
-// codes are exactly those of a float32 reference.  Both kernels stream with
-// 16-byte loads and are bandwidth-bound.
+// float bits per wave into one of 64 slots) and the quantisation, whose waves
+// each reduce the slots, form s = amax / 448 and write E4M3(v / s) with an
+// IEEE division, so the codes are exactly those of a float32 reference; its
+// first thread also stores the final amax for later kernels.  Both kernels
+// stream with 16-byte loads and are bandwidth-bound.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -28,7 +29,8 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict_
                        fmaxf(fabsf(bf16_lo(q.w)), fabsf(bf16_hi(q.w)))));
   }
   m = wave_max(m);
-  if ((threadIdx.x & (kWave - 1)) == 0 && m > 0.0f) atomic_max_nonneg(amax, m);
+  if ((threadIdx.x & (kWave - 1)) == 0 && m > 0.0f)
+    amax_slot_max(amax, blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, m);
 }
 
 __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d, float s) {
@@ -38,11 +40,15 @@ __device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d, fl
 
 // codes = E4M3(x / s), 8 bfloat16 in -> 8 codes out per thread per step.
 __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint4* __restrict__ x, int64_t n8,
-                                                         const uint32_t* __restrict__ amax,
+                                                         uint32_t* __restrict__ amax,
                                                          uint2* __restrict__ codes,
                                                          float* __restrict__ scale_out) {
-  const float s = scale_from_amax_bits(*amax);
-  if (blockIdx.x == 0 && threadIdx.x == 0 && scale_out) *scale_out = s;
+  const float m = amax_slots_reduce(amax);
+  const float s = scale_from_amax_bits(__float_as_uint(m));
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    amax[kAmaxFinal] = __float_as_uint(m);
+    if (scale_out) *scale_out = s;
+  }
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n8;
        j += (int64_t)gridDim.x * blockDim.x) {
     uint4 q = x[j];
@@ -56,9 +62,11 @@ __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint4* __restrict
 // codes = E4M3(a / s) for float32 a (n % 8 == 0), the amax came from the
 // producer of a.
 __global__ __launch_bounds__(256) void quant_f32_kernel(const float4* __restrict__ a, int64_t n8,
-                                                        const uint32_t* __restrict__ amax,
+                                                        uint32_t* __restrict__ amax,
                                                         uint2* __restrict__ codes) {
-  const float s = scale_from_amax_bits(*amax);
+  const float m = amax_slots_reduce(amax);
+  const float s = scale_from_amax_bits(__float_as_uint(m));
+  if (blockIdx.x == 0 && threadIdx.x == 0) amax[kAmaxFinal] = __float_as_uint(m);
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n8;
        j += (int64_t)gridDim.x * blockDim.x) {
     float4 p = a[2 * j], q = a[2 * j + 1];
@@ -69,8 +77,9 @@ __global__ __launch_bounds__(256) void quant_f32_kernel(const float4* __restrict
   }
 }
 
-__global__ void zero_words_kernel(uint32_t* p, int n) {
-  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+// Clears the slots of n consecutive amax blocks.
+__global__ void zero_amax_kernel(uint32_t* p, int nblocks) {
+  for (int t = threadIdx.x; t < nblocks * kAmaxSlots; t += blockDim.x) p[amax_zero_index(t)] = 0u;
 }
 
 unsigned stream_grid(int64_t n8, int num_cus) {
@@ -82,8 +91,8 @@ unsigned stream_grid(int64_t n8, int num_cus) {
 
 }  // namespace
 
-hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t stream) {
-  zero_words_kernel<<<1, 64, 0, stream>>>(p, n);
+hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream) {
+  zero_amax_kernel<<<1, 64, 0, stream>>>(p, nblocks);
   return hipGetLastError();
 }
 
@@ -95,7 +104,7 @@ hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cu
   return hipGetLastError();
 }
 
-hipError_t launch_quant_bf16(const void* x, int64_t n, const uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
                              float* scale_out, int num_cus, hipStream_t stream) {
   const int64_t n8 = n / 8;
   quant_bf16_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
@@ -103,7 +112,7 @@ hipError_t launch_quant_bf16(const void* x, int64_t n, const uint32_t* amax, uin
   return hipGetLastError();
 }
 
-hipError_t launch_quant_f32(const float* a, int64_t n, const uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream) {
   const int64_t n8 = n / 8;
   quant_f32_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(

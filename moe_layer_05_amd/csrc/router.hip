@@ -40,8 +40,10 @@ template <int VPL>   // logits per lane: ceil(E / 64)
 __global__ __launch_bounds__(256) void router_kernel(
     const float* __restrict__ logits, int64_t T, int E, int K, int renorm,
     int32_t* __restrict__ ids, float* __restrict__ wts,
-    uint32_t* __restrict__ zero_words, int n_zero) {
-  if (blockIdx.x == 0 && threadIdx.x < n_zero) zero_words[threadIdx.x] = 0u;
+    uint32_t* __restrict__ zero_amax, int n_amax) {
+  // clears the amax slots of this call's quantisations (n_amax blocks)
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_amax * kAmaxSlots)
+    zero_amax[amax_zero_index(threadIdx.x)] = 0u;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (t >= T) return;
@@ -98,8 +100,8 @@ __global__ __launch_bounds__(256) void router_kernel(
 }  // namespace
 
 hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renorm,
-                         int32_t* ids, float* wts, uint32_t* zero_words,
-                         int n_zero, hipStream_t stream) {
+                         int32_t* ids, float* wts, uint32_t* zero_amax,
+                         int n_amax, hipStream_t stream) {
   const int waves_per_block = 4;
   const int64_t blocks = (T + waves_per_block - 1) / waves_per_block;
   dim3 grid((unsigned)(blocks > 0 ? blocks : 1)), block(waves_per_block * kWave);
@@ -107,7 +109,7 @@ hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renor
 #define MOE_ROUTER_CASE(N)                                                     \
   case N:                                                                      \
     router_kernel<N><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, \
-                                                 wts, zero_words, n_zero);     \
+                                                 wts, zero_amax, n_amax);     \
     break;
   switch (vpl) {
     MOE_ROUTER_CASE(1)
@@ -116,9 +118,9 @@ hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renor
     MOE_ROUTER_CASE(8)
     MOE_ROUTER_CASE(16)
     default:
-      if (vpl == 3) { router_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, wts, zero_words, n_zero); break; }
-      if (vpl <= 8) { router_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, wts, zero_words, n_zero); break; }
-      router_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, wts, zero_words, n_zero);
+      if (vpl == 3) { router_kernel<4><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, wts, zero_amax, n_amax); break; }
+      if (vpl <= 8) { router_kernel<8><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, wts, zero_amax, n_amax); break; }
+      router_kernel<16><<<grid, block, 0, stream>>>(logits, T, E, K, renorm, ids, wts, zero_amax, n_amax);
   }
 #undef MOE_ROUTER_CASE
   return hipGetLastError();

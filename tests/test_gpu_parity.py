@@ -236,3 +236,27 @@ def test_fused_fp8_prefill_zipf_sampled():
     cfg = workloads.CONFIGS["fp8_prefill_zipf"]
     tokens = np.random.default_rng(0).choice(4096, 24, replace=False)
     run_case(cfg, 4096, "fp8", tokens=np.sort(tokens), gen_dev=DEV)
+
+
+# ------------------------------------------------------------------ determinism
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("over,T", [
+    (dict(H=2048, I=1040, E=16, K=4), 7),   # row tails in both products
+    (dict(H=144, I=48, E=6, K=3), 40),
+    (dict(), 300),
+])
+def test_fused_run_to_run_bit_identical(over, T, wdtype):
+    """The same call, repeated, gives the same bits: the combine adds in a
+    fixed order and no kernel result depends on timing."""
+    cfg = replace(TINY, name="det", **over)
+    w = _weights(cfg, wdtype, "cpu")
+    tk = workloads.make_tokens(cfg, T, seed=3)
+    x, lg = tk["x"].to(DEV), tk["logits"].to(DEV)
+    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"))
+    say("determinism", over, T, wdtype)
+    first = m(x, lg).clone()
+    for _ in range(7):
+        again = m(x, lg)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
