@@ -60,8 +60,8 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.bm = moe_fused_block_m(T, H, I, E, K, wd);
   L.nblk = max_blocks(P, E, L.bm);
   L.cap = L.nblk * L.bm;
-  L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem);
-  L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem);
+  L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem, L.bm);
+  L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem, L.bm);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   L.ids = take(P * 4);

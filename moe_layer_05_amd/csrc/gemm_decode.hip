@@ -77,6 +77,30 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The same for a run-time number of whole stages (0 <= stages < D) of L
+// loads each: the counter takes an immediate, so this branches (uniformly)
+// to the matching wait.
+template <int L, int D>
+__device__ __forceinline__ void wait_stages(int stages) {
+  static_assert((D - 1) * L <= 63, "vmcnt range");
+  switch (stages) {
+    case 1: if constexpr (D > 1) wait_vmcnt<1 * L>(); break;
+    case 2: if constexpr (D > 2) wait_vmcnt<2 * L>(); break;
+    case 3: if constexpr (D > 3) wait_vmcnt<3 * L>(); break;
+    case 4: if constexpr (D > 4) wait_vmcnt<4 * L>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// Ring depth for RA weight tiles and NSUB token tiles per wave: each wave
+// holds D * (RA + NSUB) * 4 KB of LDS, and the depth is picked so the 160 KB of
+// a compute unit keep the most weight bytes in flight (waves per unit x
+// (D - 1) x RA x 4 KB), within the 6-bit vector-memory counter.
+constexpr int ring_depth(int ra, int nsub) {
+  return nsub == 1 ? (ra == 1 ? 5 : (ra == 2 ? 4 : 3))
+                   : (nsub == 2 ? (ra == 4 ? 3 : (ra == 2 ? 3 : 4)) : 2);
+}
+
 template <bool FP8>
 struct Tile {
   // 16x16 accumulate of one 256-byte chunk: A = 16 weight rows, B = 16 tokens.
@@ -265,16 +289,21 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
         issue(d, c + D + d);
       }
     }
+    // Drain: stages hold chunks c .. c + D - 1, and ex = c_full - c - D
+    // (0 <= ex < D) chunks remain to be loaded into the stages as they free.
+    // Before consuming stage d, the stages loaded after it are the D - 1 - d
+    // later ones and the min(d, ex) refilled ones.
+    const int ex = c_full - c - D;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      wait_vmcnt<0>();
+      wait_stages<kLoads, D>(D - 1 - d + min(d, ex));
       consume(d, false, 0);
-      if (c + D + d < c_full) issue(d, c + D + d);
+      if (d < ex) issue(d, c + D + d);
     }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      if (c + D + d < c_full) {
-        wait_vmcnt<0>();
+      if (d < ex) {
+        wait_stages<kLoads, D>(ex - 1 - d);
         consume(d, false, 0);
       }
     }
@@ -282,10 +311,13 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
 #pragma unroll
     for (int d = 0; d < D; ++d)
       if (d < nc) issue(d, c_begin + d);
-    wait_vmcnt<0>();
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < nc) consume(d, false, 0);
+    for (int d = 0; d < D; ++d) {
+      if (d < nc) {
+        wait_stages<kLoads, D>(nc - 1 - d);
+        consume(d, false, 0);
+      }
+    }
   }
   // The row's partial last chunk, when this part holds it.
   if (c_end > nfull) {
@@ -364,15 +396,21 @@ hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Ring depth per (weight tiles, token tiles) of a wave: each wave holds
-// D * (RA + NSUB) * 4 KB of LDS, so the 160 KB of a compute unit keep about
-// 64 KB of weights in flight.
 template <int MODE, bool FP8, int RA>
 hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, hipStream_t stream) {
+  if (p.row_bytes <= kChunk) {
+    // one chunk per row: no ring, so the LDS holds more waves
+    switch (nsub_max) {
+      case 1: return launch_one<MODE, FP8, 1, RA, 1>(p, grid, stream);
+      case 2: return launch_one<MODE, FP8, 2, RA, 1>(p, grid, stream);
+      case 4: return launch_one<MODE, FP8, 4, RA, 1>(p, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (nsub_max) {
-    case 1: return launch_one<MODE, FP8, 1, RA, (RA == 1 ? 5 : (RA == 2 ? 4 : 1))>(p, grid, stream);
-    case 2: return launch_one<MODE, FP8, 2, RA, (RA == 1 ? 3 : (RA == 2 ? 3 : 1))>(p, grid, stream);
-    case 4: return launch_one<MODE, FP8, 4, RA, (RA == 1 ? 2 : (RA == 2 ? 2 : 1))>(p, grid, stream);
+    case 1: return launch_one<MODE, FP8, 1, RA, ring_depth(RA, 1)>(p, grid, stream);
+    case 2: return launch_one<MODE, FP8, 2, RA, ring_depth(RA, 2)>(p, grid, stream);
+    case 4: return launch_one<MODE, FP8, 4, RA, ring_depth(RA, 4)>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -386,17 +424,21 @@ hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid,
 
 }  // namespace
 
-DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes) {
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm) {
   DecodeShape s{};
   const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
+  const int nsub = bm / 16;
   if (mode == kGateUp) {
-    // rows = I: a wave owns 16 columns, i.e. 16 gate and 16 up rows.
-    s.ra = 2;
-    s.groups = (rows + 15) / 16;
+    // rows = I: a wave owns RA / 2 groups of 16 columns (16 gate and 16 up
+    // rows each); more token tiles call for more weight tiles per wave, so
+    // the weights keep most of the LDS ring.
+    s.ra = nsub == 1 ? 2 : 4;
+    s.groups = (rows + 8 * s.ra - 1) / (8 * s.ra);
     s.splits = 1;
   } else {
     // rows = H: RA 16-row tiles per wave; short rows take more tiles.
-    s.ra = row_bytes >= 1024 ? 1 : (row_bytes >= 512 ? 2 : 4);
+    if (row_bytes < 512) s.ra = 4;
+    else s.ra = nsub == 1 ? 2 : 4;
     s.groups = (rows + 16 * s.ra - 1) / (16 * s.ra);
     // Split the reduction when there are too few waves to cover the chip
     // (about 2048 in flight), keeping >= 8 chunks per part.
@@ -417,9 +459,9 @@ hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, i
   dim3 grid((unsigned)wgs);
   if (mode == kGateUp) {
     if (ra == 2) return launch_dtype<kGateUp, 2>(fp8, p, nsub_max, grid, stream);
+    if (ra == 4) return launch_dtype<kGateUp, 4>(fp8, p, nsub_max, grid, stream);
     return hipErrorInvalidValue;
   }
-  if (ra == 1) return launch_dtype<kDown, 1>(fp8, p, nsub_max, grid, stream);
   if (ra == 2) return launch_dtype<kDown, 2>(fp8, p, nsub_max, grid, stream);
   if (ra == 4) return launch_dtype<kDown, 4>(fp8, p, nsub_max, grid, stream);
   return hipErrorInvalidValue;

@@ -60,7 +60,7 @@ hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* 
 hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream);
 
-DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes);
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm);
 hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
                               hipStream_t stream);
 
