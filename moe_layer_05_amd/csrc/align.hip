@@ -14,6 +14,12 @@
 // in the whole pair list is the running count of earlier chunks plus the
 // counts of earlier waves plus the in-wave rank.  Every step is a pure
 // function of the input order, so the layout is deterministic and stable.
+//
+// Split form (used by the fused forward at prefill sizes): experts with at
+// least `thr` pairs are laid out in a second, separate layout padded to a
+// larger block size, for the tiled products; the others keep the small
+// blocks.  With thr beyond the pair count every expert is small and the
+// result is the plain layout above.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -23,15 +29,46 @@ namespace {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 
+struct AlignOut {
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_post_pad;
+  int BM;
+};
+
+// Block-wide exclusive scan of one int per thread (1024 threads); returns the
+// exclusive prefix and stores the total in *total (every thread).
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int n = __shfl_up(incl, o);
+    if (lane >= o) incl += n;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kAlignWaves; ++w) {
+    if (w < wave) before += wsum[w];
+    all += wsum[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int BM,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ num_post_pad, int32_t* __restrict__ rank) {
+    const int32_t* __restrict__ ids, int P, int E, AlignOut small, AlignOut big, int thr,
+    int32_t* __restrict__ rank) {
   extern __shared__ int smem[];
   int* cnt = smem;                                   // [E] running counts
-  int* seg = smem + E;                               // [E] segment starts
-  int* wsum = smem + 2 * E;                          // [16] scan scratch
-  uint8_t* wc = reinterpret_cast<uint8_t*>(smem + 2 * E + kAlignWaves);  // [16][E]
+  int* seg = smem + E;                               // [E] segment starts (small)
+  int* segb = smem + 2 * E;                          // [E] segment starts (big)
+  int* wsum = smem + 3 * E;                          // [16] scan scratch
+  uint8_t* wc = reinterpret_cast<uint8_t*>(smem + 3 * E + kAlignWaves);  // [16][E]
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -71,42 +108,64 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     __syncthreads();
   }
 
-  // Exclusive scan of the padded counts over experts (E <= 1024: one each).
-  const int my_pad = (tid < E) ? (cnt[tid] + BM - 1) / BM * BM : 0;
-  int incl = my_pad;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int n = __shfl_up(incl, o);
-    if (lane >= o) incl += n;
+  // Exclusive scans of the padded counts over experts (E <= 1024: one each),
+  // one per layout.
+  const int c_e = (tid < E) ? cnt[tid] : 0;
+  const bool is_big = c_e >= thr;
+  const int pad_s = (!is_big) ? (c_e + small.BM - 1) / small.BM * small.BM : 0;
+  const int pad_b = is_big ? (c_e + big.BM - 1) / big.BM * big.BM : 0;
+  int tot_s, tot_b;
+  const int start_s = block_exclusive_scan(pad_s, wsum, &tot_s);
+  const int start_b = block_exclusive_scan(pad_b, wsum, &tot_b);
+  if (tid < E) {
+    seg[tid] = start_s;
+    segb[tid] = start_b;
   }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  const int start = before + incl - my_pad;
-  if (tid < E) seg[tid] = start;
-  if (tid == kAlignThreads - 1) num_post_pad[0] = before + incl;
-  if (tid < E && my_pad > 0) {
-    const int c = cnt[tid];
-    for (int b = 0; b < my_pad / BM; ++b) block_expert[start / BM + b] = tid;
-    for (int p = start + c; p < start + my_pad; ++p) sorted_ids[p] = P;
+  if (tid == 0) {
+    small.num_post_pad[0] = tot_s;
+    if (big.num_post_pad) big.num_post_pad[0] = tot_b;
+  }
+  if (tid < E && pad_s > 0) {
+    for (int b = 0; b < pad_s / small.BM; ++b) small.block_expert[start_s / small.BM + b] = tid;
+    for (int q = start_s + c_e; q < start_s + pad_s; ++q) small.sorted_ids[q] = P;
+  }
+  if (tid < E && pad_b > 0) {
+    for (int b = 0; b < pad_b / big.BM; ++b) big.block_expert[start_b / big.BM + b] = tid;
+    for (int q = start_b + c_e; q < start_b + pad_b; ++q) big.sorted_ids[q] = P;
   }
   __syncthreads();
 
-  for (int i = tid; i < P; i += kAlignThreads) sorted_ids[seg[ids[i]] + rank[i]] = i;
+  for (int i = tid; i < P; i += kAlignThreads) {
+    const int e = ids[i];
+    if (cnt[e] >= thr) big.sorted_ids[segb[e] + rank[i]] = i;
+    else small.sorted_ids[seg[e] + rank[i]] = i;
+  }
 }
 
 }  // namespace
 
 size_t align_lds_bytes(int E) {
-  return (size_t)(2 * E + kAlignWaves) * sizeof(int) + (size_t)kAlignWaves * E;
+  return (size_t)(3 * E + kAlignWaves) * sizeof(int) + (size_t)kAlignWaves * E;
 }
 
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream) {
-  align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(
-      ids, P, E, BM, sorted_ids, block_expert, num_post_pad, rank);
+  AlignOut small{sorted_ids, block_expert, num_post_pad, BM};
+  AlignOut big{nullptr, nullptr, nullptr, 256};
+  align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, small, big,
+                                                                 0x7FFFFFFF, rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_align_split(const int32_t* ids, int P, int E, int BM_small,
+                              int32_t* sorted_small, int32_t* bexp_small, int32_t* npp_small,
+                              int BM_big, int32_t* sorted_big, int32_t* bexp_big,
+                              int32_t* npp_big, int thr, int32_t* rank, hipStream_t stream) {
+  AlignOut small{sorted_small, bexp_small, npp_small, BM_small};
+  AlignOut big{sorted_big, bexp_big, npp_big, BM_big};
+  align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, small, big, thr,
+                                                                 rank);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 // C ABI of the fused MoE layer (declared in include/moe.h): host-side argument
 // checks, workspace layout and the launch sequence.  No device memory is
 // allocated and nothing synchronises the host.
+#include <algorithm>
 #include <mutex>
 
 #include "moe.h"
@@ -45,23 +46,43 @@ int64_t max_blocks(int64_t P, int E, int bm) {
   return P / bm + active;
 }
 
+// Experts with at least this many pairs take the tiled products when the
+// call is large enough to have such experts (prefill); the rest keep the
+// weight-streaming kernels.
+constexpr int kTileThreshold = 16;
+
 struct FusedLayout {
   size_t ids, wts, sorted, bexp, npp, rank, scal, qx, a, qa, dw, total;
+  size_t sorted_t, bexp_t, npp_t;     // tiled layout (prefill)
   int bm;
   int64_t cap, nblk;
+  bool tiled;
+  int64_t cap_t, nblk_t;
   DecodeShape gu, dn;
 };
+
+bool use_tiles(int64_t T, int E, int K) {
+  return T >= 256 && T * (int64_t)K >= 32LL * E;
+}
 
 FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   FusedLayout L{};
   const int64_t P = T * K;
   const bool fp8 = wd == MOE_FP8_E4M3;
   const int welem = fp8 ? 1 : 2;
-  L.bm = moe_fused_block_m(T, H, I, E, K, wd);
+  L.tiled = use_tiles(T, E, K);
+  L.bm = L.tiled ? 16 : moe_fused_block_m(T, H, I, E, K, wd);
   L.nblk = max_blocks(P, E, L.bm);
   L.cap = L.nblk * L.bm;
+  if (L.tiled) {
+    const int bmt = tile_block_m();
+    const int64_t big_experts = std::min<int64_t>(E, P / kTileThreshold);
+    L.nblk_t = P / bmt + big_experts;
+    L.cap_t = L.nblk_t * bmt;
+  }
   L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem, L.bm);
   L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem, L.bm);
+  if (L.tiled) L.dn.splits = 1;          // the tiled products write one part
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   L.ids = take(P * 4);
@@ -69,6 +90,9 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.sorted = take(L.cap * 4);
   L.bexp = take(L.nblk * 4);
   L.npp = take(4);
+  L.sorted_t = take(L.tiled ? L.cap_t * 4 : 0);
+  L.bexp_t = take(L.tiled ? L.nblk_t * 4 : 0);
+  L.npp_t = take(4);
   L.rank = take(P * 4);
   L.scal = take(2 * kAmaxWords * 4);     // amax blocks of x and of a
   L.qx = take(fp8 ? (size_t)T * H : 0);
@@ -238,7 +262,14 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   if (e == hipSuccess && fp8) e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
   // a2
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
-  if (e == hipSuccess) e = launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
+  int32_t* sorted_t = reinterpret_cast<int32_t*>(ws + L.sorted_t);
+  int32_t* bexp_t = reinterpret_cast<int32_t*>(ws + L.bexp_t);
+  int32_t* npp_t = reinterpret_cast<int32_t*>(ws + L.npp_t);
+  if (e == hipSuccess) {
+    e = L.tiled ? launch_align_split(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
+                                     sorted_t, bexp_t, npp_t, kTileThreshold, rank, stream)
+                : launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
+  }
 
   // a3 + a4
   GemmParams g{};
@@ -263,6 +294,16 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.a_out = abuf;
     g.a_amax = fp8 ? amax_a : nullptr;
     e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, stream);
+    if (e == hipSuccess && L.tiled) {
+      GemmParams t = g;
+      t.sorted_ids = sorted_t;
+      t.block_expert = bexp_t;
+      t.num_post_pad = npp_t;
+      t.BM = tile_block_m();
+      t.groups = tile_groups(kGateUp, I);
+      t.splits = 1;
+      e = launch_gemm_tile(kGateUp, fp8, t, L.nblk_t, stream);
+    }
   }
   // intermediate quantisation (FP8)
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_INTER_QUANT, stream);
@@ -284,6 +325,16 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.dw_split_stride = (int64_t)P * H;
     g.topk_w = wts;
     e = launch_gemm_decode(kDown, fp8, g, L.dn.ra, L.nblk, stream);
+    if (e == hipSuccess && L.tiled) {
+      GemmParams t = g;
+      t.sorted_ids = sorted_t;
+      t.block_expert = bexp_t;
+      t.num_post_pad = npp_t;
+      t.BM = tile_block_m();
+      t.groups = tile_groups(kDown, H);
+      t.splits = 1;
+      e = launch_gemm_tile(kDown, fp8, t, L.nblk_t, stream);
+    }
   }
   // a6
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, stream);

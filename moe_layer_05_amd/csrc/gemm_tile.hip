@@ -1,0 +1,319 @@
+// a3-a6 for large token blocks (prefill): a grouped, LDS-pipelined MFMA GEMM
+// over blocks of 256 tokens of one expert.
+//
+// An expert that receives hundreds of tokens turns its products into dense
+// matrix work; grouped GEMMs over the experts' token blocks are what the layer
+// is made of (kongchang.com page, "Swap-AB": grouped and batched GEMMs are
+// abundant in MoE).  The expert weight rows still take the MFMA row side, as
+// in the decode kernel (toolboxkart.tech page, section 1; aib.vote page,
+// second paragraph), so each lane's four accumulators are four consecutive
+// output features and the epilogue stores them as one vector.  The epilogues
+// apply the dequantisation scales, SiLU-and-mul, and the routing weight in the
+// same pass (aib.vote page, third paragraph).
+//
+// Workgroup tile: 256 weight rows x 256 tokens, 8 waves in a 2 x 4 grid, each
+// wave 128 x 64 = 8 x 4 MFMA 16x16 tiles (fp8: one 16x16x128 per tile and
+// k-step; bf16: two 16x16x32).  Two waves per SIMD: while one waits for its
+// LDS reads, the other issues MFMAs.  The k-step is 128 bytes of the reduction
+// dimension; weight and token tiles of a k-step (32 KB each) move HBM/L2 ->
+// LDS with direct-to-LDS loads, two stages deep (128 KB), one barrier per
+// k-step.  LDS rows are 128 bytes with the 16-byte granule index XOR-ed by
+// (row & 7), which keeps the MFMA-layout reads free of bank conflicts.
+//
+// Gate/up: the 256 weight rows are 128 gate rows and the 128 up rows of the
+// same intermediate columns, so SiLU(g) * u is formed in registers.  Down:
+// 256 consecutive rows of W2.  The token rows are gathered through the sorted
+// pair ids; padding slots read a valid row and their columns are not stored.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTM = 256;            // weight rows per workgroup tile
+constexpr int kTN = 256;            // tokens per workgroup tile (= block size)
+constexpr int kBK = 128;            // bytes of the reduction dimension per k-step
+constexpr int kStageBytes = (kTM + kTN) * kBK;   // 64 KB
+constexpr int kTileLds = 2 * kStageBytes;        // 128 KB
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Four 16-byte LDS reads and the wait for them.
+__device__ __forceinline__ void lds_read4(uint4 (&d)[4], uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %5\n"
+      "ds_read_b128 %2, %6\n"
+      "ds_read_b128 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+template <bool FP8>
+__device__ __forceinline__ v4f tile_mma(const uint4 (&a)[2], const uint4 (&b)[2], v4f acc) {
+  if constexpr (FP8) {
+    v8i av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+              (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+    v8i bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+              (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[0]),
+                                                  __builtin_bit_cast(v8bf, b[0]), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[1]),
+                                                   __builtin_bit_cast(v8bf, b[1]), acc, 0, 0, 0);
+  }
+}
+
+// Eight 16-byte LDS reads and the wait for them.
+__device__ __forceinline__ void lds_read8(uint4 (&d)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %9\n"
+      "ds_read_b128 %2, %10\n"
+      "ds_read_b128 %3, %11\n"
+      "ds_read_b128 %4, %12\n"
+      "ds_read_b128 %5, %13\n"
+      "ds_read_b128 %6, %14\n"
+      "ds_read_b128 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]),
+        "=&v"(d[6]), "=&v"(d[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
+
+constexpr int kWaves = 8;
+constexpr int kLoadsPerWave = 32 / kWaves;       // 1 KB loads per tile (A or B) per wave
+
+template <int MODE, bool FP8>
+__global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g4 = lane >> 4;
+
+  // The grid covers the capacity bound; the routed tiles are the first G.
+  // Workgroups are handed to the 8 XCDs in turn, so tile t is chosen to make
+  // each XCD's tiles consecutive in the (block, column tile) order: a block's
+  // token rows are then reused from that XCD's L2, and every XCD gets an
+  // equal share of the routed tiles.
+  const int G = (p.num_post_pad[0] / kTN) * p.groups;
+  if ((int)blockIdx.x >= G) return;                // whole workgroup: before any barrier
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+  const int q = G >> 3, rr = G & 7;
+  const int t = xcd * q + min(xcd, rr) + idx;
+  const int b = t / p.groups;
+  const int n = t - b * p.groups;
+  const int e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
+  const int32_t* blk = p.sorted_ids + (int64_t)b * kTN;
+
+  const int row_bytes = (int)p.row_bytes;
+  const int nfull = row_bytes / kBK;
+  const int nk = (row_bytes + kBK - 1) / kBK;
+
+  // ---- loads into LDS.  Load instruction i (1 KB) of a tile covers tile
+  // rows 8i .. 8i + 7: lane -> row 8i + (lane >> 3), LDS position lane & 7,
+  // which holds the row's 16-byte granule (lane & 7) ^ (lane >> 3).  Wave w
+  // issues loads i = 4w .. 4w + 3 of the weight tile and of the token tile.
+  const int lrow = lane >> 3;
+  const uint32_t gq = (uint32_t)(((lane & 7) ^ lrow) * 16);
+  const uint8_t* wexp = p.W + (int64_t)e * p.w_expert_bytes;
+  const uint8_t* a_src[kLoadsPerWave];
+  const uint8_t* b_src[kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int r = (kLoadsPerWave * wave + i) * 8 + lrow;   // tile row 0..255
+    int wr;
+    if constexpr (MODE == kGateUp) {
+      const int col = n * 128 + (r & 127);
+      wr = (col < p.I) ? ((r < 128) ? col : p.I + col) : 0;
+    } else {
+      const int h = n * kTM + r;
+      wr = (h < p.H) ? h : 0;
+    }
+    a_src[i] = wexp + (int64_t)wr * row_bytes;
+    const int32_t pair = blk[r];
+    const int64_t brow = pair < p.P ? (int64_t)(pair / p.b_row_div) : 0;
+    b_src[i] = p.B + brow * row_bytes;
+  }
+  uint8_t* a_lds = smem + wave * kLoadsPerWave * 1024;                 // + stage * kStageBytes
+  uint8_t* b_lds = smem + kTM * kBK + wave * kLoadsPerWave * 1024;
+
+  auto issue = [&](int stage, int k) {
+    const uint32_t off = (uint32_t)k * kBK;
+    const bool tail = k >= nfull;
+    const uint32_t o = (!tail || off + gq < (uint32_t)row_bytes) ? off + gq : 0u;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + o),
+                                       (lds_void*)(a_lds + stage * kStageBytes + i * 1024), 16,
+                                       0, 2);
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + o),
+                                       (lds_void*)(b_lds + stage * kStageBytes + i * 1024), 16,
+                                       0, 0);
+  };
+
+  // ---- MFMA-layout reads: lane holds row l16 of a 16-row tile and the 32
+  // bytes of granules 2 g4 and 2 g4 + 1 of the k-step.
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t sw = (uint32_t)(l16 & 7);
+  const uint32_t r0 = lds_addr(smem) + l16 * kBK + (((2 * g4) ^ sw) * 16);
+  const uint32_t r1 = lds_addr(smem) + l16 * kBK + (((2 * g4 + 1) ^ sw) * 16);
+  // first row of weight tile ai / token tile bj of this wave inside a stage
+  auto a_row = [&](int ai) -> int {
+    if constexpr (MODE == kGateUp) return (ai < 4 ? 0 : 128) + 64 * wm + 16 * (ai & 3);
+    else return 128 * wm + 16 * ai;
+  };
+  const int b_row0 = kTM + 64 * wn;
+
+  v4f acc[8][4];
+#pragma unroll
+  for (int ai = 0; ai < 8; ++ai)
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) acc[ai][bj] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int stage, bool tail, uint32_t off) {
+    const uint32_t sb = (uint32_t)stage * kStageBytes;
+    uint4 bt[8];                                   // token tile bj: bt[2 bj], bt[2 bj + 1]
+    uint32_t ba[8];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const uint32_t o = sb + (uint32_t)(b_row0 + 16 * bj) * kBK;
+      ba[2 * bj] = r0 + o;
+      ba[2 * bj + 1] = r1 + o;
+    }
+    lds_read8(bt, ba);
+    if (tail) {
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        if (off + (2 * g4) * 16 >= (uint32_t)row_bytes) bt[2 * bj] = make_uint4(0, 0, 0, 0);
+        if (off + (2 * g4 + 1) * 16 >= (uint32_t)row_bytes) bt[2 * bj + 1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ai = 0; ai < 8; ai += 2) {
+      uint4 at[4];
+      const uint32_t o0 = sb + (uint32_t)a_row(ai) * kBK;
+      const uint32_t o1 = sb + (uint32_t)a_row(ai + 1) * kBK;
+      lds_read4(at, r0 + o0, r1 + o0, r0 + o1, r1 + o1);
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        const uint4 bb[2] = {bt[2 * bj], bt[2 * bj + 1]};
+        const uint4 a0[2] = {at[0], at[1]};
+        const uint4 a1[2] = {at[2], at[3]};
+        acc[ai][bj] = tile_mma<FP8>(a0, bb, acc[ai][bj]);
+        acc[ai + 1][bj] = tile_mma<FP8>(a1, bb, acc[ai + 1][bj]);
+      }
+    }
+  };
+
+  issue(0, 0);
+  for (int k = 0; k < nk; ++k) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of stage k
+    __syncthreads();                                   // all waves: stage k in, stage k-1 read
+    if (k + 1 < nk) issue((k + 1) & 1, k + 1);
+    compute(k & 1, k >= nfull, (uint32_t)k * kBK);
+  }
+
+  // ------------------------------------------------------------ epilogue
+  float scale = 1.0f;
+  if constexpr (FP8) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[e];
+  if constexpr (MODE == kGateUp) {
+    float local_max = 0.0f;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int32_t pair = blk[64 * wn + 16 * bj + l16];
+      if (pair >= p.P) continue;
+#pragma unroll
+      for (int ai = 0; ai < 4; ++ai) {
+        const int col = n * 128 + 64 * wm + 16 * ai + 4 * g4;
+        if (col >= p.I) continue;
+        float av[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float gt = acc[ai][bj][v] * scale;
+          const float up = acc[ai + 4][bj][v] * scale;
+          av[v] = gt / (1.0f + __expf(-gt)) * up;
+          local_max = fmaxf(local_max, fabsf(av[v]));
+        }
+        if constexpr (FP8) {
+          float* dst = static_cast<float*>(p.a_out) + (int64_t)pair * p.I + col;
+          *reinterpret_cast<float4*>(dst) = make_float4(av[0], av[1], av[2], av[3]);
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.a_out) + (int64_t)pair * p.I + col;
+          uint2 pk;
+          pk.x = f32_to_bf16_bits(av[0]) | (f32_to_bf16_bits(av[1]) << 16);
+          pk.y = f32_to_bf16_bits(av[2]) | (f32_to_bf16_bits(av[3]) << 16);
+          *reinterpret_cast<uint2*>(dst) = pk;
+        }
+      }
+    }
+    if constexpr (FP8) {
+      local_max = wave_max(local_max);
+      if (lane == 0 && local_max > 0.0f)
+        amax_slot_max(p.a_amax, (uint32_t)(blockIdx.x * kWaves + wave), local_max);
+    }
+  } else {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int32_t pair = blk[64 * wn + 16 * bj + l16];
+      if (pair >= p.P) continue;
+      const float sc = scale * p.topk_w[pair];
+#pragma unroll
+      for (int ai = 0; ai < 8; ++ai) {
+        const int h = n * kTM + 128 * wm + 16 * ai + 4 * g4;
+        if (h >= p.H) continue;
+        float* dst = p.dw + (int64_t)pair * p.H + h;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(acc[ai][bj][0] * sc, acc[ai][bj][1] * sc, acc[ai][bj][2] * sc,
+                        acc[ai][bj][3] * sc);
+      }
+    }
+  }
+}
+
+template <int MODE, bool FP8>
+hipError_t launch_tile(const GemmParams& p, dim3 grid, hipStream_t stream) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FP8>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kTileLds);
+  if (attr != hipSuccess) return attr;
+  moe_gemm_tile_kernel<MODE, FP8><<<grid, dim3(64 * kWaves), kTileLds, stream>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int tile_block_m() { return kTN; }
+
+int tile_groups(int mode, int rows) {
+  return mode == kGateUp ? (rows + 127) / 128 : (rows + kTM - 1) / kTM;
+}
+
+hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
+                            hipStream_t stream) {
+  if (p.BM != kTN) return hipErrorInvalidValue;
+  const int64_t wgs = nblk_cap * p.groups;
+  if (wgs <= 0) return hipSuccess;
+  if (wgs > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)wgs);
+  if (mode == kGateUp)
+    return fp8 ? launch_tile<kGateUp, true>(p, grid, stream)
+               : launch_tile<kGateUp, false>(p, grid, stream);
+  return fp8 ? launch_tile<kDown, true>(p, grid, stream)
+             : launch_tile<kDown, false>(p, grid, stream);
+}
+
+}  // namespace moe

@@ -51,6 +51,12 @@ size_t align_lds_bytes(int E);
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream);
+// Two layouts at once: experts with >= thr pairs in blocks of BM_big, the
+// others in blocks of BM_small.
+hipError_t launch_align_split(const int32_t* ids, int P, int E, int BM_small,
+                              int32_t* sorted_small, int32_t* bexp_small, int32_t* npp_small,
+                              int BM_big, int32_t* sorted_big, int32_t* bexp_big,
+                              int32_t* npp_big, int thr, int32_t* rank, hipStream_t stream);
 
 hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream);
 hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
@@ -63,6 +69,13 @@ hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* 
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm);
 hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
                               hipStream_t stream);
+
+// Tiled products for large token blocks (BM = tile_block_m()); groups are
+// the column tiles per block.
+int tile_block_m();
+int tile_groups(int mode, int rows);
+hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
+                            hipStream_t stream);
 
 hipError_t launch_combine(const float* dw, int splits, int64_t T, int K, int H, void* out,
                           int num_cus, hipStream_t stream);

@@ -260,3 +260,14 @@ def test_fused_run_to_run_bit_identical(over, T, wdtype):
         again = m(x, lg)
         torch.cuda.synchronize()
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("over,T", [
+    (dict(H=2048, I=1040, E=16, K=4), 512),   # tiled experts + small ones, column and row tails
+    (dict(H=1152, I=320, E=32, K=6), 700),
+])
+def test_fused_prefill_sizes(over, T, wdtype):
+    """Calls large enough that the hot experts take the tiled products."""
+    cfg = replace(TINY, name="pf_" + "_".join(f"{k}{v}" for k, v in over.items()), **over)
+    run_case(cfg, T, wdtype)
