@@ -71,8 +71,10 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   const bool fp8 = wd == MOE_FP8_E4M3;
   const int welem = fp8 ? 1 : 2;
   L.tiled = use_tiles(T, E, K);
-  L.bm = L.tiled ? 16 : moe_fused_block_m(T, H, I, E, K, wd);
-  L.nblk = max_blocks(P, E, L.bm);
+  L.bm = L.tiled ? kTileThreshold : moe_fused_block_m(T, H, I, E, K, wd);
+  // In the split layout every small expert has fewer than kTileThreshold =
+  // BM pairs, so it takes exactly one block.
+  L.nblk = L.tiled ? std::min<int64_t>(E, P) : max_blocks(P, E, L.bm);
   L.cap = L.nblk * L.bm;
   if (L.tiled) {
     const int bmt = tile_block_m();
@@ -302,7 +304,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       t.BM = tile_block_m();
       t.groups = tile_groups(kGateUp, I);
       t.splits = 1;
-      e = launch_gemm_tile(kGateUp, fp8, t, L.nblk_t, stream);
+      e = launch_gemm_tile(kGateUp, fp8, t, L.nblk_t, cus, stream);
     }
   }
   // intermediate quantisation (FP8)
@@ -333,7 +335,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       t.BM = tile_block_m();
       t.groups = tile_groups(kDown, H);
       t.splits = 1;
-      e = launch_gemm_tile(kDown, fp8, t, L.nblk_t, stream);
+      e = launch_gemm_tile(kDown, fp8, t, L.nblk_t, cus, stream);
     }
   }
   // a6

@@ -46,6 +46,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return code | sign;
 }
 
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) and
+// exponential; for very negative z, e^-z is +inf and the result is -0.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // Activation scale from an amax stored as float bits: amax / 448, 1 if zero.
 __device__ __forceinline__ float scale_from_amax_bits(uint32_t amax_bits) {
   float amax = __uint_as_float(amax_bits);

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
         for (int v = 0; v < 4; ++v) {
           const float gt = acc[2 * cg][s][v] * scale;
           const float up = acc[2 * cg + 1][s][v] * scale;
-          av[v] = gt / (1.0f + __expf(-gt)) * up;
+          av[v] = silu_fast(gt) * up;
           local_max = fmaxf(local_max, fabsf(av[v]));
         }
         if constexpr (FP8) {

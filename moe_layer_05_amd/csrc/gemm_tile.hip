@@ -18,12 +18,17 @@
 // dimension; weight and token tiles of a k-step (32 KB each) move HBM/L2 ->
 // LDS with direct-to-LDS loads, two stages deep (128 KB), one barrier per
 // k-step.  LDS rows are 128 bytes with the 16-byte granule index XOR-ed by
-// (row & 7), which keeps the MFMA-layout reads free of bank conflicts.
+// (row & 7); a lane of lane group g4 takes granules g4 and g4 + 4 of its row
+// (any fixed assignment of k positions works, as A and B share it), which the
+// hardware reads without bank conflicts (granule pairs 2 g4, 2 g4 + 1 would
+// conflict on half the cycles).
 //
 // Gate/up: the 256 weight rows are 128 gate rows and the 128 up rows of the
 // same intermediate columns, so SiLU(g) * u is formed in registers.  Down:
 // 256 consecutive rows of W2.  The token rows are gathered through the sorted
 // pair ids; padding slots read a valid row and their columns are not stored.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -102,20 +107,30 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // The grid covers the capacity bound; the routed tiles are the first G.
-  // Workgroups are handed to the 8 XCDs in turn, so tile t is chosen to make
-  // each XCD's tiles consecutive in the (block, column tile) order: a block's
-  // token rows are then reused from that XCD's L2, and every XCD gets an
-  // equal share of the routed tiles.
-  const int G = (p.num_post_pad[0] / kTN) * p.groups;
-  if ((int)blockIdx.x >= G) return;                // whole workgroup: before any barrier
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-  const int q = G >> 3, rr = G & 7;
-  const int t = xcd * q + min(xcd, rr) + idx;
-  const int b = t / p.groups;
-  const int n = t - b * p.groups;
-  const int e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
-  const int32_t* blk = p.sorted_ids + (int64_t)b * kTN;
+  // Persistent: one workgroup per compute unit walks a list of tiles.  The
+  // routed blocks are cut into 8 contiguous ranges, one per XCD (workgroups
+  // are handed to the XCDs in turn, blockIdx & 7).  An XCD's tiles are walked
+  // in panels of 4 blocks x 8 column tiles and its workgroups take them in
+  // turn, so the 32 tiles running at once on an XCD read 4 token slices and 8
+  // weight slices per k-step from its L2 (a 2 x 16 arrangement would read 18).
+  constexpr int kPB = 4, kPN = 8;
+  const int nb = p.num_post_pad[0] / kTN;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, nj = gridDim.x >> 3;
+  const int b0 = (xcd * nb) >> 3, b1 = ((xcd + 1) * nb) >> 3;
+  const int cnt_x = (b1 - b0) * p.groups;
+  int it = j;
+  if (it >= cnt_x) return;                         // whole workgroup: before any barrier
+  auto tile_of = [&](int l, int& b, int& n) {
+    const int gw = p.groups;
+    const int bp = l / (kPB * gw);
+    const int bpw = min(kPB, (b1 - b0) - bp * kPB);
+    const int rem = l - bp * kPB * gw;
+    const int np = rem / (bpw * kPN);
+    const int npw = min(kPN, gw - np * kPN);
+    const int inner = rem - np * bpw * kPN;
+    b = b0 + bp * kPB + inner / npw;
+    n = np * kPN + inner % npw;
+  };
 
   const int row_bytes = (int)p.row_bytes;
   const int nfull = row_bytes / kBK;
@@ -127,28 +142,40 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   // issues loads i = 4w .. 4w + 3 of the weight tile and of the token tile.
   const int lrow = lane >> 3;
   const uint32_t gq = (uint32_t)(((lane & 7) ^ lrow) * 16);
-  const uint8_t* wexp = p.W + (int64_t)e * p.w_expert_bytes;
-  const uint8_t* a_src[kLoadsPerWave];
-  const uint8_t* b_src[kLoadsPerWave];
-#pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int r = (kLoadsPerWave * wave + i) * 8 + lrow;   // tile row 0..255
-    int wr;
-    if constexpr (MODE == kGateUp) {
-      const int col = n * 128 + (r & 127);
-      wr = (col < p.I) ? ((r < 128) ? col : p.I + col) : 0;
-    } else {
-      const int h = n * kTM + r;
-      wr = (h < p.H) ? h : 0;
-    }
-    a_src[i] = wexp + (int64_t)wr * row_bytes;
-    const int32_t pair = blk[r];
-    const int64_t brow = pair < p.P ? (int64_t)(pair / p.b_row_div) : 0;
-    b_src[i] = p.B + brow * row_bytes;
-  }
   uint8_t* a_lds = smem + wave * kLoadsPerWave * 1024;                 // + stage * kStageBytes
   uint8_t* b_lds = smem + kTM * kBK + wave * kLoadsPerWave * 1024;
 
+  // A tile's identity (kept for its epilogue) and the load addresses of the
+  // tile being loaded (replaced by the next tile's during the last k-step).
+  struct Tile {
+    int n, e;
+    const int32_t* blk;
+  };
+  const uint8_t* a_src[kLoadsPerWave];
+  const uint8_t* b_src[kLoadsPerWave];
+  auto setup = [&](int l, Tile& s) {
+    int b;
+    tile_of(l, b, s.n);
+    s.e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
+    s.blk = p.sorted_ids + (int64_t)b * kTN;
+    const uint8_t* wexp = p.W + (int64_t)s.e * p.w_expert_bytes;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int r = (kLoadsPerWave * wave + i) * 8 + lrow;   // tile row 0..255
+      int wr;
+      if constexpr (MODE == kGateUp) {
+        const int col = s.n * 128 + (r & 127);
+        wr = (col < p.I) ? ((r < 128) ? col : p.I + col) : 0;
+      } else {
+        const int h = s.n * kTM + r;
+        wr = (h < p.H) ? h : 0;
+      }
+      a_src[i] = wexp + (int64_t)wr * row_bytes;
+      const int32_t pair = s.blk[r];
+      const int64_t brow = pair < p.P ? (int64_t)(pair / p.b_row_div) : 0;
+      b_src[i] = p.B + brow * row_bytes;
+    }
+  };
   auto issue = [&](int stage, int k) {
     const uint32_t off = (uint32_t)k * kBK;
     const bool tail = k >= nfull;
@@ -166,11 +193,11 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   };
 
   // ---- MFMA-layout reads: lane holds row l16 of a 16-row tile and the 32
-  // bytes of granules 2 g4 and 2 g4 + 1 of the k-step.
+  // bytes of granules g4 and g4 + 4 of the k-step.
   const int wm = wave & 1, wn = wave >> 1;
   const uint32_t sw = (uint32_t)(l16 & 7);
-  const uint32_t r0 = lds_addr(smem) + l16 * kBK + (((2 * g4) ^ sw) * 16);
-  const uint32_t r1 = lds_addr(smem) + l16 * kBK + (((2 * g4 + 1) ^ sw) * 16);
+  const uint32_t r0 = lds_addr(smem) + l16 * kBK + ((g4 ^ sw) * 16);
+  const uint32_t r1 = lds_addr(smem) + l16 * kBK + (((g4 + 4) ^ sw) * 16);
   // first row of weight tile ai / token tile bj of this wave inside a stage
   auto a_row = [&](int ai) -> int {
     if constexpr (MODE == kGateUp) return (ai < 4 ? 0 : 128) + 64 * wm + 16 * (ai & 3);
@@ -179,11 +206,6 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   const int b_row0 = kTM + 64 * wn;
 
   v4f acc[8][4];
-#pragma unroll
-  for (int ai = 0; ai < 8; ++ai)
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) acc[ai][bj] = v4f{0.f, 0.f, 0.f, 0.f};
-
   auto compute = [&](int stage, bool tail, uint32_t off) {
     const uint32_t sb = (uint32_t)stage * kStageBytes;
     uint4 bt[8];                                   // token tile bj: bt[2 bj], bt[2 bj + 1]
@@ -198,8 +220,8 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     if (tail) {
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) {
-        if (off + (2 * g4) * 16 >= (uint32_t)row_bytes) bt[2 * bj] = make_uint4(0, 0, 0, 0);
-        if (off + (2 * g4 + 1) * 16 >= (uint32_t)row_bytes) bt[2 * bj + 1] = make_uint4(0, 0, 0, 0);
+        if (off + g4 * 16 >= (uint32_t)row_bytes) bt[2 * bj] = make_uint4(0, 0, 0, 0);
+        if (off + (g4 + 4) * 16 >= (uint32_t)row_bytes) bt[2 * bj + 1] = make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -219,68 +241,93 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     }
   };
 
-  issue(0, 0);
-  for (int k = 0; k < nk; ++k) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of stage k
-    __syncthreads();                                   // all waves: stage k in, stage k-1 read
-    if (k + 1 < nk) issue((k + 1) & 1, k + 1);
-    compute(k & 1, k >= nfull, (uint32_t)k * kBK);
-  }
-
   // ------------------------------------------------------------ epilogue
-  float scale = 1.0f;
-  if constexpr (FP8) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[e];
-  if constexpr (MODE == kGateUp) {
-    float local_max = 0.0f;
+  auto epilogue = [&](const Tile& s) {
+    float scale = 1.0f;
+    if constexpr (FP8) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[s.e];
+    if constexpr (MODE == kGateUp) {
+      float local_max = 0.0f;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int32_t pair = blk[64 * wn + 16 * bj + l16];
-      if (pair >= p.P) continue;
+      for (int bj = 0; bj < 4; ++bj) {
+        const int32_t pair = s.blk[64 * wn + 16 * bj + l16];
+        if (pair >= p.P) continue;
 #pragma unroll
-      for (int ai = 0; ai < 4; ++ai) {
-        const int col = n * 128 + 64 * wm + 16 * ai + 4 * g4;
-        if (col >= p.I) continue;
-        float av[4];
+        for (int ai = 0; ai < 4; ++ai) {
+          const int col = s.n * 128 + 64 * wm + 16 * ai + 4 * g4;
+          if (col >= p.I) continue;
+          float av[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float gt = acc[ai][bj][v] * scale;
-          const float up = acc[ai + 4][bj][v] * scale;
-          av[v] = gt / (1.0f + __expf(-gt)) * up;
-          local_max = fmaxf(local_max, fabsf(av[v]));
+          for (int v = 0; v < 4; ++v) {
+            const float gt = acc[ai][bj][v] * scale;
+            const float up = acc[ai + 4][bj][v] * scale;
+            av[v] = silu_fast(gt) * up;
+            local_max = fmaxf(local_max, fabsf(av[v]));
+          }
+          if constexpr (FP8) {
+            float* dst = static_cast<float*>(p.a_out) + (int64_t)pair * p.I + col;
+            *reinterpret_cast<float4*>(dst) = make_float4(av[0], av[1], av[2], av[3]);
+          } else {
+            uint16_t* dst = static_cast<uint16_t*>(p.a_out) + (int64_t)pair * p.I + col;
+            uint2 pk;
+            pk.x = f32_to_bf16_bits(av[0]) | (f32_to_bf16_bits(av[1]) << 16);
+            pk.y = f32_to_bf16_bits(av[2]) | (f32_to_bf16_bits(av[3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = pk;
+          }
         }
-        if constexpr (FP8) {
-          float* dst = static_cast<float*>(p.a_out) + (int64_t)pair * p.I + col;
-          *reinterpret_cast<float4*>(dst) = make_float4(av[0], av[1], av[2], av[3]);
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(p.a_out) + (int64_t)pair * p.I + col;
-          uint2 pk;
-          pk.x = f32_to_bf16_bits(av[0]) | (f32_to_bf16_bits(av[1]) << 16);
-          pk.y = f32_to_bf16_bits(av[2]) | (f32_to_bf16_bits(av[3]) << 16);
-          *reinterpret_cast<uint2*>(dst) = pk;
+      }
+      if constexpr (FP8) {
+        local_max = wave_max(local_max);
+        if (lane == 0 && local_max > 0.0f)
+          amax_slot_max(p.a_amax, (uint32_t)(blockIdx.x * kWaves + wave), local_max);
+      }
+    } else {
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        const int32_t pair = s.blk[64 * wn + 16 * bj + l16];
+        if (pair >= p.P) continue;
+        const float sc = scale * p.topk_w[pair];
+#pragma unroll
+        for (int ai = 0; ai < 8; ++ai) {
+          const int h = s.n * kTM + 128 * wm + 16 * ai + 4 * g4;
+          if (h >= p.H) continue;
+          float* dst = p.dw + (int64_t)pair * p.H + h;
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(acc[ai][bj][0] * sc, acc[ai][bj][1] * sc, acc[ai][bj][2] * sc,
+                          acc[ai][bj][3] * sc);
         }
       }
     }
-    if constexpr (FP8) {
-      local_max = wave_max(local_max);
-      if (lane == 0 && local_max > 0.0f)
-        amax_slot_max(p.a_amax, (uint32_t)(blockIdx.x * kWaves + wave), local_max);
-    }
-  } else {
+  };
+
+  // ---- the walk: during a tile's last k-step the first stage of the next
+  // tile is loaded, so a tile's start and its epilogue overlap with loads.
+  Tile cur, nxt;
+  setup(it, cur);
+  issue(0, 0);
+  int stage = 0;
+  for (;;) {
+    const int it_next = it + nj;
+    const bool has_next = it_next < cnt_x;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int32_t pair = blk[64 * wn + 16 * bj + l16];
-      if (pair >= p.P) continue;
-      const float sc = scale * p.topk_w[pair];
+    for (int ai = 0; ai < 8; ++ai)
 #pragma unroll
-      for (int ai = 0; ai < 8; ++ai) {
-        const int h = n * kTM + 128 * wm + 16 * ai + 4 * g4;
-        if (h >= p.H) continue;
-        float* dst = p.dw + (int64_t)pair * p.H + h;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(acc[ai][bj][0] * sc, acc[ai][bj][1] * sc, acc[ai][bj][2] * sc,
-                        acc[ai][bj][3] * sc);
+      for (int bj = 0; bj < 4; ++bj) acc[ai][bj] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < nk; ++k) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of this stage
+      __syncthreads();                                   // all waves: stage in, other stage read
+      if (k + 1 < nk) {
+        issue(stage ^ 1, k + 1);
+      } else if (has_next) {
+        setup(it_next, nxt);
+        issue(stage ^ 1, 0);
       }
+      compute(stage, k >= nfull, (uint32_t)k * kBK);
+      stage ^= 1;
     }
+    epilogue(cur);
+    if (!has_next) break;
+    cur = nxt;
+    it = it_next;
   }
 }
 
@@ -303,11 +350,13 @@ int tile_groups(int mode, int rows) {
 }
 
 hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
-                            hipStream_t stream) {
+                            int num_cus, hipStream_t stream) {
   if (p.BM != kTN) return hipErrorInvalidValue;
-  const int64_t wgs = nblk_cap * p.groups;
-  if (wgs <= 0) return hipSuccess;
-  if (wgs > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;
+  const int64_t tiles = nblk_cap * p.groups;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;
+  // one workgroup per compute unit (a multiple of 8: one share per XCD)
+  int64_t wgs = std::min<int64_t>(std::max(num_cus / 8, 1), (tiles + 7) / 8) * 8;
   dim3 grid((unsigned)wgs);
   if (mode == kGateUp)
     return fp8 ? launch_tile<kGateUp, true>(p, grid, stream)

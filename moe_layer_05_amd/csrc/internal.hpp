@@ -75,7 +75,7 @@ hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, i
 int tile_block_m();
 int tile_groups(int mode, int rows);
 hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
-                            hipStream_t stream);
+                            int num_cus, hipStream_t stream);
 
 hipError_t launch_combine(const float* dw, int splits, int64_t T, int K, int H, void* out,
                           int num_cus, hipStream_t stream);
