@@ -16,10 +16,12 @@ sub-batch (``cpu_baseline``).
 """
 
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -49,6 +51,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work the cpu_baseline sample aims at")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: read two rocprofv3 --pmc result folders (FETCH_SIZE, "
+                         "WRITE_SIZE) of this same command with --copy-calib-mib, and store "
+                         "the dominant kernel's HBM bytes per call in profiles/traffic.json")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before the layer, copy this many MiB once with a plain "
                          "device copy (a known-size reference for HBM counters)")
@@ -77,6 +83,63 @@ def load_traffic(workload, T, kernel):
     if not rec or rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
         return None
     return rec.get("bytes_per_launch")
+
+
+STAGE_KERNELS = {"gate_up": re.compile(r"moe_gemm_\w+_kernel<0,"),
+                 "down": re.compile(r"moe_gemm_\w+_kernel<1,")}
+
+
+def read_counter(folder, counter):
+    """{dispatch id: (kernel name, summed value)} of one rocprofv3 --pmc run."""
+    import csv
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {folder}, found {len(files)}")
+    out = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def record_traffic(args):
+    """HBM bytes per call of the dominant stage from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    calibration kernel that reads and writes a known number of bytes."""
+    if not args.copy_calib_mib:
+        raise SystemExit("--record-traffic needs the --copy-calib-mib of the profiled runs")
+    from moe_layer_05_amd import workloads
+    cfg = workloads.CONFIGS[args.workload]
+    T = args.T or (4096 if args.workload == "fp8_prefill_zipf" else max(cfg.Ts))
+    n = float(args.copy_calib_mib << 20)
+    rec = {"kernel": "gate_up", "source_digest": source_digest()}
+    for folder, counter, key in ((args.record_traffic[0], "FETCH_SIZE", "fetch"),
+                                 (args.record_traffic[1], "WRITE_SIZE", "write")):
+        disp = read_counter(folder, counter)
+        calib = [v for name, v in disp.values() if "bitwise_not" in name]
+        calls = sum(1 for name, _ in disp.values() if "router_kernel" in name)
+        stage = [v for name, v in disp.values() if STAGE_KERNELS["gate_up"].search(name)]
+        if len(calib) != 1 or calls == 0 or not stage:
+            raise SystemExit(f"{folder}: calibration {len(calib)}, calls {calls}, "
+                             f"stage dispatches {len(stage)}")
+        factor = calib[0] * 1024.0 / n           # counter bytes per real byte
+        rec[f"{key}_factor"] = round(factor, 4)
+        rec[f"{key}_bytes_per_call"] = round(sum(stage) * 1024.0 / factor / calls)
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"]
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            db = json.load(fh)
+    except (OSError, ValueError):
+        db = {}
+    db[f"{cfg.name}/T{T}"] = rec
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({f"{cfg.name}/T{T}": rec}))
 
 
 class Work:
@@ -198,6 +261,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.record_traffic:
+        record_traffic(args)
+        return
     import numpy as np
     import torch
 
@@ -220,7 +286,7 @@ def main():
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)       # one elementwise kernel: n bytes in, n out
         torch.cuda.synchronize()
         del src, dst
         log(f"copy calibration: {args.copy_calib_mib} MiB read + written once")

@@ -26,7 +26,8 @@
 // Gate/up: the 256 weight rows are 128 gate rows and the 128 up rows of the
 // same intermediate columns, so SiLU(g) * u is formed in registers.  Down:
 // 256 consecutive rows of W2.  The token rows are gathered through the sorted
-// pair ids; padding slots read a valid row and their columns are not stored.
+// pair ids; padding slots read a valid row and their columns are not stored,
+// and a wave whose 64 token slots are all padding skips its MFMAs.
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -150,6 +151,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   struct Tile {
     int n, e;
     const int32_t* blk;
+    int nsub;                                      // 16-token tiles of this wave holding a pair
   };
   const uint8_t* a_src[kLoadsPerWave];
   const uint8_t* b_src[kLoadsPerWave];
@@ -158,6 +160,11 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     tile_of(l, b, s.n);
     s.e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
     s.blk = p.sorted_ids + (int64_t)b * kTN;
+    {
+      // the pairs of a block are a prefix of it, the rest is padding
+      const uint64_t live = __ballot(s.blk[64 * (wave >> 1) + lane] < p.P);
+      s.nsub = __builtin_amdgcn_readfirstlane((__popcll(live) + 15) >> 4);
+    }
     const uint8_t* wexp = p.W + (int64_t)s.e * p.w_expert_bytes;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
@@ -226,15 +233,15 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     }
 #pragma unroll
     for (int ai = 0; ai < 8; ai += 2) {
-      uint4 at[4];
+      uint4 cur[4];
       const uint32_t o0 = sb + (uint32_t)a_row(ai) * kBK;
       const uint32_t o1 = sb + (uint32_t)a_row(ai + 1) * kBK;
-      lds_read4(at, r0 + o0, r1 + o0, r0 + o1, r1 + o1);
+      lds_read4(cur, r0 + o0, r1 + o0, r0 + o1, r1 + o1);
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) {
         const uint4 bb[2] = {bt[2 * bj], bt[2 * bj + 1]};
-        const uint4 a0[2] = {at[0], at[1]};
-        const uint4 a1[2] = {at[2], at[3]};
+        const uint4 a0[2] = {cur[0], cur[1]};
+        const uint4 a1[2] = {cur[2], cur[3]};
         acc[ai][bj] = tile_mma<FP8>(a0, bb, acc[ai][bj]);
         acc[ai + 1][bj] = tile_mma<FP8>(a1, bb, acc[ai + 1][bj]);
       }
@@ -321,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
         setup(it_next, nxt);
         issue(stage ^ 1, 0);
       }
-      compute(stage, k >= nfull, (uint32_t)k * kBK);
+      if (__builtin_amdgcn_readfirstlane(cur.nsub) > 0) compute(stage, k >= nfull, (uint32_t)k * kBK);
       stage ^= 1;
     }
     epilogue(cur);
