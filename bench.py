@@ -62,12 +62,15 @@ def parse():
 
 
 def source_digest():
-    """sha256 of the HIP sources; traffic counters are valid for one digest."""
+    """sha256 of the HIP sources with comments and blank lines removed; traffic
+    counters are valid for one digest (a comment edit keeps them)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "moe_layer_05_amd", "csrc")
     for f in sorted(os.listdir(d)):
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+        with open(os.path.join(d, f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+        h.update(f.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,9 +22,14 @@
 //
 // Decode is a weight stream: every byte of an active expert is read once and
 // used by at most a few tokens.  The kernel is shaped for that:
-//  - weight loads are non-temporal (the data is not reused, and streaming it
-//    past the last-level cache raises the sustained read rate of HBM3E);
-//  - each wave keeps D chunks of its rows in flight in a register ring;
+//  - both operands move HBM/L2 -> LDS with direct-to-LDS loads (no VGPR
+//    staging); weight loads are non-temporal (the data is not reused, and
+//    streaming it past the last-level cache raises the sustained read rate of
+//    HBM3E), activation rows (x, x codes, a, a codes: small, shared by all row
+//    groups of an expert) go through the caches;
+//  - each wave owns a ring of D chunk stages in LDS and keeps D - 1 of them in
+//    flight; it waits on its own vector-memory counter, so no workgroup
+//    barrier is needed (one wave per workgroup);
 //  - the unit of work is one wave: (block b, row group g, k-split s), where a
 //    row group is RA 16-row MFMA tiles; the grid is not persistent: one wave
 //    per unit of the capacity bound, so the hardware dispatcher balances the
@@ -33,8 +38,6 @@
 //  - the down product may split its reduction dimension I into S parts; each
 //    part writes its own weighted partial rows and the combine adds the parts
 //    in a fixed order, so results stay deterministic.
-// Activation rows (x, x codes, a, a codes) are small and shared by all row
-// groups of an expert; they are loaded through the caches.
 #include "device_common.hpp"
 #include "internal.hpp"
 
