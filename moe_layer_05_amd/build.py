@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoemi.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "router.hip", "align.hip", "quant.hip", "gemm_decode.hip", "gemm_tile.hip",
+SOURCES = ["api.hip", "router.hip", "align.hip", "front.hip", "quant.hip", "gemm_decode.hip", "gemm_tile.hip",
            "combine.hip"]
 
 ARCH = "gfx950"

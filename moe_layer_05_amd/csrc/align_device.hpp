@@ -1,0 +1,166 @@
+// a2 (device side): align -- stable counting sort of the token-expert pairs by expert, each
+// expert's run padded to a multiple of block_m with the sentinel T*K.
+//
+// Grouping the tokens of each expert is what lets every expert run one
+// grouped matrix product over a variable number of tokens (kongchang.com page,
+// "Why MoE Inference Is So Sensitive to Kernel Engineering": the number of
+// tokens each expert receives is variable; "Swap-AB": grouped GEMMs).
+//
+// One workgroup of 1024 threads (16 waves) walks the pairs in chunks of 1024.
+// Inside a chunk, each lane finds the lanes of its wave holding the same
+// expert with one ballot per bit of the expert id (a wave-level multisplit),
+// so its rank among equal experts of its wave is a popcount; the per-wave
+// counts go to LDS (one writer per wave and expert, no atomics), and the rank
+// in the whole pair list is the running count of earlier chunks plus the
+// counts of earlier waves plus the in-wave rank.  Every step is a pure
+// function of the input order, so the layout is deterministic and stable.
+//
+// Split form (used by the fused forward at prefill sizes): experts with at
+// least `thr` pairs are laid out in a second, separate layout padded to a
+// larger block size, for the tiled products; the others keep the small
+// blocks.  With thr beyond the pair count every expert is small and the
+// result is the plain layout above.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace moe {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+
+struct AlignOut {
+  int32_t* sorted_ids;
+  int32_t* block_expert;
+  int32_t* num_post_pad;
+  int BM;
+};
+
+// Block-wide exclusive scans of two ints per thread (1024 threads) sharing
+// one pair of barriers; returns the exclusive prefixes and the totals (every
+// thread).  `wsum` holds 2 * kAlignWaves ints.
+__device__ __forceinline__ int2 block_exclusive_scan2(int v0, int v1, int* wsum, int2* total) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int i0 = wave_inclusive_sum_dpp(v0);
+  const int i1 = wave_inclusive_sum_dpp(v1);
+  __syncthreads();
+  if (lane == kWave - 1) {
+    wsum[wave] = i0;
+    wsum[kAlignWaves + wave] = i1;
+  }
+  __syncthreads();
+  int2 before = make_int2(0, 0), all = make_int2(0, 0);
+#pragma unroll
+  for (int w = 0; w < kAlignWaves; ++w) {
+    const int a = wsum[w], b = wsum[kAlignWaves + w];
+    if (w < wave) {
+      before.x += a;
+      before.y += b;
+    }
+    all.x += a;
+    all.y += b;
+  }
+  *total = all;
+  return make_int2(before.x + i0 - v0, before.y + i1 - v1);
+}
+
+// The whole align step by one workgroup of kAlignThreads threads; `smem`
+// holds align_lds_words(E) ints.  `ids` may have been written earlier in the
+// same kernel by this workgroup (a workgroup barrier must separate them).
+__device__ __forceinline__ void align_block(const int32_t* ids, int P, int E, AlignOut small,
+                                            AlignOut big, int thr, int32_t* __restrict__ rank,
+                                            int* smem) {
+  int* cnt = smem;                                   // [E] running counts
+  int* seg = smem + E;                               // [E] segment starts (small)
+  int* segb = smem + 2 * E;                          // [E] segment starts (big)
+  int* wsum = smem + 3 * E;                          // [2][16] scan scratch
+  uint8_t* wc = reinterpret_cast<uint8_t*>(smem + 3 * E + 2 * kAlignWaves);  // [16][E]
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int nbits = (E > 1) ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+
+  for (int e = tid; e < E; e += kAlignThreads) cnt[e] = 0;
+
+  int e0 = 0, r0 = 0;                                // this thread's pair of the first chunk
+  for (int base = 0; base < P; base += kAlignThreads) {
+    for (int j = tid; j < kAlignWaves * E; j += kAlignThreads) wc[j] = 0;
+    __syncthreads();
+    const int i = base + tid;
+    const bool valid = i < P;
+    const int e = valid ? ids[i] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    const int rw = __popcll(peers & lt_mask);
+    if (valid && rw == 0) wc[wave * E + e] = (uint8_t)__popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int r = cnt[e] + rw;
+      for (int w = 0; w < wave; ++w) r += wc[w * E + e];
+      if (base == 0) {
+        e0 = e;
+        r0 = r;
+      } else {
+        rank[i] = r;
+      }
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kAlignThreads) {
+      int s = 0;
+#pragma unroll
+      for (int w = 0; w < kAlignWaves; ++w) s += wc[w * E + ee];
+      cnt[ee] += s;
+    }
+    __syncthreads();
+  }
+
+  // Exclusive scans of the padded counts over experts (E <= 1024: one each),
+  // one per layout.
+  const int c_e = (tid < E) ? cnt[tid] : 0;
+  const bool is_big = c_e >= thr;
+  const int pad_s = (!is_big) ? (c_e + small.BM - 1) / small.BM * small.BM : 0;
+  const int pad_b = is_big ? (c_e + big.BM - 1) / big.BM * big.BM : 0;
+  int2 tot;
+  const int2 start = block_exclusive_scan2(pad_s, pad_b, wsum, &tot);
+  const int start_s = start.x, start_b = start.y, tot_s = tot.x, tot_b = tot.y;
+  if (tid < E) {
+    seg[tid] = start_s;
+    segb[tid] = start_b;
+  }
+  if (tid == 0) {
+    small.num_post_pad[0] = tot_s;
+    if (big.num_post_pad) big.num_post_pad[0] = tot_b;
+  }
+  if (tid < E && pad_s > 0) {
+    for (int b = 0; b < pad_s / small.BM; ++b) small.block_expert[start_s / small.BM + b] = tid;
+    for (int q = start_s + c_e; q < start_s + pad_s; ++q) small.sorted_ids[q] = P;
+  }
+  if (tid < E && pad_b > 0) {
+    for (int b = 0; b < pad_b / big.BM; ++b) big.block_expert[start_b / big.BM + b] = tid;
+    for (int q = start_b + c_e; q < start_b + pad_b; ++q) big.sorted_ids[q] = P;
+  }
+  __syncthreads();
+
+  for (int i = tid; i < P; i += kAlignThreads) {
+    const int e = i < kAlignThreads ? e0 : ids[i];
+    const int r = i < kAlignThreads ? r0 : rank[i];
+    if (cnt[e] >= thr) big.sorted_ids[segb[e] + r] = i;
+    else small.sorted_ids[seg[e] + r] = i;
+  }
+}
+
+// LDS of align_block: counts, two segment starts, scan scratch (ints) and the
+// per-wave counts (bytes).
+constexpr size_t align_lds_words(int E) {
+  return (size_t)(3 * E + 2 * kAlignWaves) + ((size_t)kAlignWaves * E + 3) / 4;
+}
+
+}  // namespace moe

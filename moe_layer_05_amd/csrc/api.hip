@@ -253,24 +253,34 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   const int cus = num_cus();
   const int welem = fp8 ? 1 : 2;
 
-  // a1 (also clears the amax slots of x and a for this call)
-  hipError_t e = mark(ev, MOE_STAGE_ROUTE, stream);
-  if (e == hipSuccess)
-    e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x, fp8 ? 2 : 0,
-                               stream);
-  // a0
-  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
-  if (e == hipSuccess && fp8) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
-  if (e == hipSuccess && fp8) e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
-  // a2
-  if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
   int32_t* sorted_t = reinterpret_cast<int32_t*>(ws + L.sorted_t);
   int32_t* bexp_t = reinterpret_cast<int32_t*>(ws + L.bexp_t);
   int32_t* npp_t = reinterpret_cast<int32_t*>(ws + L.npp_t);
-  if (e == hipSuccess) {
-    e = L.tiled ? launch_align_split(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
-                                     sorted_t, bexp_t, npp_t, kTileThreshold, rank, stream)
-                : launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
+  hipError_t e = mark(ev, MOE_STAGE_ROUTE, stream);
+  if (!L.tiled && front_fits(T, H, K, fp8)) {
+    // a1 + a0 + a2 in one launch; the act-quant and align stages are empty
+    if (e == hipSuccess)
+      e = launch_front(a->router_logits, T, E, K, a->renormalize, ids, wts, fp8, a->x, H, amax_x,
+                       amax_a, qx, L.bm, sorted, bexp, npp, rank, stream);
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
+  } else {
+    // a1 (also clears the amax slots of x and a for this call)
+    if (e == hipSuccess)
+      e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x,
+                        fp8 ? 2 : 0, stream);
+    // a0
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
+    if (e == hipSuccess && fp8) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
+    if (e == hipSuccess && fp8)
+      e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
+    // a2
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
+    if (e == hipSuccess) {
+      e = L.tiled ? launch_align_split(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
+                                       sorted_t, bexp_t, npp_t, kTileThreshold, rank, stream)
+                  : launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
+    }
   }
 
   // a3 + a4

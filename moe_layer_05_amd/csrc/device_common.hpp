@@ -46,6 +46,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return code | sign;
 }
 
+// Four codes E4M3(v / s) in one word, first value in the low byte.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d, float s) {
+  return f32_to_e4m3(a / s) | (f32_to_e4m3(b / s) << 8) | (f32_to_e4m3(c / s) << 16) |
+         (f32_to_e4m3(d / s) << 24);
+}
+
 // silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) and
 // exponential; for very negative z, e^-z is +inf and the result is -0.
 __device__ __forceinline__ float silu_fast(float z) {
@@ -72,6 +78,84 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Whole-wave reductions with DPP row operations: each step moves data between
+// lanes inside the register file (a few cycles, no LDS round trip).  Steps:
+// swap neighbours, swap pairs, mirror halves of 8, mirror rows of 16 (every
+// lane then holds its row's result), then broadcast lane 15 of a row into the
+// next row and lane 31 into rows 2 and 3; lane 63 ends with the full result,
+// which is read back as a wave-uniform value.  Every lane of the wave must be
+// active.
+namespace dpp {
+constexpr int kSwap1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kSwap2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror
+constexpr int kMirror = 0x140;      // row_mirror
+constexpr int kBcast15 = 0x142;     // row_bcast:15 (rows 1 and 3 written)
+constexpr int kBcast31 = 0x143;     // row_bcast:31 (rows 2 and 3 written)
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t move(uint32_t v) {
+  // lanes outside the written rows keep their own value
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+}
+}  // namespace dpp
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce_dpp(uint32_t v, Op op) {
+  v = op(v, dpp::move<dpp::kSwap1, 0xF>(v));
+  v = op(v, dpp::move<dpp::kSwap2, 0xF>(v));
+  v = op(v, dpp::move<dpp::kHalfMirror, 0xF>(v));
+  v = op(v, dpp::move<dpp::kMirror, 0xF>(v));
+  v = op(v, dpp::move<dpp::kBcast15, 0xA>(v));
+  v = op(v, dpp::move<dpp::kBcast31, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// row of 16 (lanes without a source add 0), then the row totals carried into
+// the following rows.  Every lane of the wave must be active.
+__device__ __forceinline__ int wave_inclusive_sum_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, dpp::kBcast15, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, dpp::kBcast31, 0xC, 0xF, false);
+  return v;
+}
+
+// max of non-negative or any floats (IEEE fmaxf), sum of floats (the order of
+// the additions is fixed by the steps above)
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  return __uint_as_float(wave_reduce_dpp(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  return __uint_as_float(wave_reduce_dpp(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+
+// max of 64-bit unsigned keys
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  auto step = [&](uint32_t olo, uint32_t ohi) {
+    const bool gt = ohi > hi || (ohi == hi && olo > lo);
+    lo = gt ? olo : lo;
+    hi = gt ? ohi : hi;
+  };
+  step(dpp::move<dpp::kSwap1, 0xF>(lo), dpp::move<dpp::kSwap1, 0xF>(hi));
+  step(dpp::move<dpp::kSwap2, 0xF>(lo), dpp::move<dpp::kSwap2, 0xF>(hi));
+  step(dpp::move<dpp::kHalfMirror, 0xF>(lo), dpp::move<dpp::kHalfMirror, 0xF>(hi));
+  step(dpp::move<dpp::kMirror, 0xF>(lo), dpp::move<dpp::kMirror, 0xF>(hi));
+  step(dpp::move<dpp::kBcast15, 0xA>(lo), dpp::move<dpp::kBcast15, 0xA>(hi));
+  step(dpp::move<dpp::kBcast31, 0xC>(lo), dpp::move<dpp::kBcast31, 0xC>(hi));
+  lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
+  hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // ---------------------------------------------------------------- amax
 
 // A per-tensor amax is gathered in kAmaxSlots words, each on its own 128-byte
@@ -94,10 +178,11 @@ __device__ __forceinline__ int amax_zero_index(int t) {
   return (t / kAmaxSlots) * kAmaxWords + (t % kAmaxSlots) * kAmaxStride;
 }
 
-// The maximum over all slots of an amax block, in every lane of the wave.
+// The maximum over all slots of an amax block, in every lane of the wave
+// (every lane active).
 __device__ __forceinline__ float amax_slots_reduce(const uint32_t* block) {
   const int lane = threadIdx.x & (kWave - 1);
-  return wave_max(__uint_as_float(block[lane * kAmaxStride]));
+  return wave_max_dpp(__uint_as_float(block[lane * kAmaxStride]));
 }
 
 }  // namespace moe

@@ -38,6 +38,8 @@
 //  - the down product may split its reduction dimension I into S parts; each
 //    part writes its own weighted partial rows and the combine adds the parts
 //    in a fixed order, so results stay deterministic.
+#include <cmath>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -427,28 +429,64 @@ hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid,
 
 }  // namespace
 
+namespace {
+
+// Waves of one shape that the chip holds at once: one wave per workgroup with
+// D * (RA + NSUB) 4 KB LDS tiles, 160 KB of LDS per compute unit, 256 units.
+int64_t resident_waves(int ra, int nsub, int64_t row_bytes) {
+  const int d = row_bytes <= kChunk ? 1 : ring_depth(ra, nsub);
+  const int per_cu = (160 * 1024) / (d * (ra + nsub) * kTileBytes);
+  return 256LL * (per_cu > 0 ? per_cu : 1);
+}
+
+// Busy fraction of the rounds a grid of `units` waves takes (the last round
+// may be partly empty).
+double round_fill(int64_t units, int64_t resident) {
+  const double r = (double)units / (double)resident;
+  return r / std::ceil(r);
+}
+
+}  // namespace
+
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm) {
   DecodeShape s{};
   const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
   const int nsub = bm / 16;
+  // RA = 2 or 4 weight tiles per wave.  Short rows make short waves, where
+  // more of them in flight wins: RA = 2.  With long rows a partly empty last
+  // round of resident waves costs a whole wave time, so the other RA is taken
+  // when its grid fills the rounds clearly better (small grids).
+  auto pick = [&](int pref, auto units_of) {
+    if (nchunks < 24) return 2;
+    const int alt = 6 - pref;
+    const double fp = round_fill(units_of(pref), resident_waves(pref, nsub, row_bytes));
+    const double fa = round_fill(units_of(alt), resident_waves(alt, nsub, row_bytes));
+    return fa > fp + 0.05 ? alt : pref;
+  };
   if (mode == kGateUp) {
     // rows = I: a wave owns RA / 2 groups of 16 columns (16 gate and 16 up
     // rows each); more token tiles call for more weight tiles per wave, so
     // the weights keep most of the LDS ring.
-    s.ra = nsub == 1 ? 2 : 4;
+    auto units = [&](int ra) { return nblk_cap * ((rows + 8 * ra - 1) / (8 * ra)); };
+    s.ra = pick(nsub == 1 ? 2 : 4, units);
     s.groups = (rows + 8 * s.ra - 1) / (8 * s.ra);
     s.splits = 1;
   } else {
-    // rows = H: RA 16-row tiles per wave; short rows take more tiles.
-    if (row_bytes < 512) s.ra = 4;
-    else s.ra = nsub == 1 ? 2 : 4;
+    // rows = H: RA 16-row tiles per wave; short rows take more tiles.  Split
+    // the reduction when there are too few waves to cover the chip (about
+    // 2048 in flight), keeping >= 8 chunks per part.
+    auto splits_of = [&](int ra) {
+      const int64_t units = nblk_cap * ((rows + 16 * ra - 1) / (16 * ra));
+      int sp = 1;
+      while (units * sp < 2048 && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
+      return sp;
+    };
+    auto units = [&](int ra) {
+      return nblk_cap * ((rows + 16 * ra - 1) / (16 * ra)) * splits_of(ra);
+    };
+    s.ra = row_bytes < 512 ? 4 : pick(nsub == 1 ? 2 : 4, units);
     s.groups = (rows + 16 * s.ra - 1) / (16 * s.ra);
-    // Split the reduction when there are too few waves to cover the chip
-    // (about 2048 in flight), keeping >= 8 chunks per part.
-    const int64_t units = nblk_cap * s.groups;
-    int sp = 1;
-    while (units * sp < 2048 && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
-    s.splits = sp;
+    s.splits = splits_of(s.ra);
   }
   return s;
 }

@@ -58,6 +58,16 @@ hipError_t launch_align_split(const int32_t* ids, int P, int E, int BM_small,
                               int BM_big, int32_t* sorted_big, int32_t* bexp_big,
                               int32_t* npp_big, int thr, int32_t* rank, hipStream_t stream);
 
+// a1 + a0 + a2 by one workgroup for small batches (front_fits): routing,
+// (FP8) the codes of x with the final amax word, the amax slots of a cleared,
+// and the align layout with block size BM.
+bool front_fits(int64_t T, int H, int K, bool fp8);
+hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm, int32_t* ids,
+                        float* wts, bool fp8, const void* x, int H, uint32_t* amax_x,
+                        uint32_t* amax_a, uint8_t* qx, int BM, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
+                        hipStream_t stream);
+
 hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream);
 hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
                             hipStream_t stream);

@@ -28,14 +28,9 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict_
     m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(q.z)), fabsf(bf16_hi(q.z))),
                        fmaxf(fabsf(bf16_lo(q.w)), fabsf(bf16_hi(q.w)))));
   }
-  m = wave_max(m);
+  m = wave_max_dpp(m);
   if ((threadIdx.x & (kWave - 1)) == 0 && m > 0.0f)
     amax_slot_max(amax, blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, m);
-}
-
-__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d, float s) {
-  return f32_to_e4m3(a / s) | (f32_to_e4m3(b / s) << 8) | (f32_to_e4m3(c / s) << 16) |
-         (f32_to_e4m3(d / s) << 24);
 }
 
 // codes = E4M3(x / s), 8 bfloat16 in -> 8 codes out per thread per step.
@@ -53,8 +48,8 @@ __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint4* __restrict
        j += (int64_t)gridDim.x * blockDim.x) {
     uint4 q = x[j];
     uint2 o;
-    o.x = pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
-    o.y = pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
+    o.x = e4m3_pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
+    o.y = e4m3_pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
     codes[j] = o;
   }
 }
@@ -71,8 +66,8 @@ __global__ __launch_bounds__(256) void quant_f32_kernel(const float4* __restrict
        j += (int64_t)gridDim.x * blockDim.x) {
     float4 p = a[2 * j], q = a[2 * j + 1];
     uint2 o;
-    o.x = pack4(p.x, p.y, p.z, p.w, s);
-    o.y = pack4(q.x, q.y, q.z, q.w, s);
+    o.x = e4m3_pack4(p.x, p.y, p.z, p.w, s);
+    o.y = e4m3_pack4(q.x, q.y, q.z, q.w, s);
     codes[j] = o;
   }
 }
