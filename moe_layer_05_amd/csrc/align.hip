@@ -12,7 +12,137 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   align_block(ids, P, E, small, big, thr, rank, smem);
 }
 
+// ---- Multi-workgroup form, for many pairs.  (1) Each workgroup ranks the
+// pairs of its chunk of kAlignThreads among equal experts (the same wave
+// multisplit as align_block) and writes the chunk's per-expert counts;
+// (2) one workgroup turns the counts into per-chunk offsets (in place) and
+// lays out both padded layouts; (3) each workgroup scatters its chunk.  The
+// position of a pair is a pure function of the input order, so the result
+// equals the one-workgroup form exactly.
+
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ rank) {
+  extern __shared__ int smem[];
+  uint8_t* wc = reinterpret_cast<uint8_t*>(smem);   // [16][E] per-wave counts
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int nbits = (E > 1) ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+  for (int j = tid; j < kAlignWaves * E; j += kAlignThreads) wc[j] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * kAlignThreads + tid;
+  const bool valid = i < P;
+  const int e = valid ? ids[i] : 0;
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rw = __popcll(peers & lt_mask);
+  if (valid && rw == 0) wc[wave * E + e] = (uint8_t)__popcll(peers);
+  __syncthreads();
+  if (valid) {
+    int r = rw;
+    for (int w = 0; w < wave; ++w) r += wc[w * E + e];
+    rank[i] = r;                                     // rank inside the chunk
+  }
+  for (int ee = tid; ee < E; ee += kAlignThreads) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kAlignWaves; ++w) c += wc[w * E + ee];
+    counts[(int64_t)blockIdx.x * E + ee] = c;
+  }
+}
+
+// counts [C][E] -> exclusive offsets over the chunks (in place); seg [3][E]
+// receives the small and big segment starts and the per-expert totals.
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
+    int32_t* __restrict__ counts, int C, int E, int P, AlignOut small, AlignOut big, int thr,
+    int32_t* __restrict__ seg) {
+  __shared__ int wsum[2 * kAlignWaves];
+  const int tid = threadIdx.x;
+  int c_e = 0;
+  if (tid < E) {
+    constexpr int kBatch = 32;                       // loads in flight per thread
+    for (int c0 = 0; c0 < C; c0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        v[k] = c0 + k < C ? counts[(int64_t)(c0 + k) * E + tid] : 0;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (c0 + k < C) counts[(int64_t)(c0 + k) * E + tid] = c_e;
+        c_e += v[k];
+      }
+    }
+  }
+  const bool is_big = c_e >= thr;
+  const int pad_s = (tid < E && !is_big) ? (c_e + small.BM - 1) / small.BM * small.BM : 0;
+  const int pad_b = (tid < E && is_big) ? (c_e + big.BM - 1) / big.BM * big.BM : 0;
+  int2 tot;
+  const int2 start = block_exclusive_scan2(pad_s, pad_b, wsum, &tot);
+  if (tid < E) {
+    seg[tid] = start.x;
+    seg[E + tid] = start.y;
+    seg[2 * E + tid] = c_e;
+  }
+  if (tid == 0) {
+    small.num_post_pad[0] = tot.x;
+    big.num_post_pad[0] = tot.y;
+  }
+  if (tid < E && pad_s > 0) {
+    for (int b = 0; b < pad_s / small.BM; ++b) small.block_expert[start.x / small.BM + b] = tid;
+    for (int q = start.x + c_e; q < start.x + pad_s; ++q) small.sorted_ids[q] = P;
+  }
+  if (tid < E && pad_b > 0) {
+    for (int b = 0; b < pad_b / big.BM; ++b) big.block_expert[start.y / big.BM + b] = tid;
+    for (int q = start.y + c_e; q < start.y + pad_b; ++q) big.sorted_ids[q] = P;
+  }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int P, int E, const int32_t* __restrict__ offs,
+    const int32_t* __restrict__ seg, const int32_t* __restrict__ rank, AlignOut small,
+    AlignOut big, int thr) {
+  const int i = blockIdx.x * kAlignThreads + threadIdx.x;
+  if (i >= P) return;
+  const int e = ids[i];
+  const int r = offs[(int64_t)blockIdx.x * E + e] + rank[i];
+  if (seg[2 * E + e] >= thr) big.sorted_ids[seg[E + e] + r] = i;
+  else small.sorted_ids[seg[e] + r] = i;
+}
+
 }  // namespace
+
+size_t align_multi_workspace_bytes(int P, int E) {
+  const size_t C = ((size_t)P + kAlignThreads - 1) / kAlignThreads;
+  return (C * E + 3 * (size_t)E) * sizeof(int32_t);
+}
+
+hipError_t launch_align_split_multi(const int32_t* ids, int P, int E, int BM_small,
+                                    int32_t* sorted_small, int32_t* bexp_small,
+                                    int32_t* npp_small, int BM_big, int32_t* sorted_big,
+                                    int32_t* bexp_big, int32_t* npp_big, int thr, int32_t* rank,
+                                    int32_t* scratch, hipStream_t stream) {
+  AlignOut small{sorted_small, bexp_small, npp_small, BM_small};
+  AlignOut big{sorted_big, bexp_big, npp_big, BM_big};
+  const int C = (P + kAlignThreads - 1) / kAlignThreads;
+  int32_t* counts = scratch;                         // [C][E]
+  int32_t* seg = scratch + (size_t)C * E;            // [3][E]
+  align_count_kernel<<<C, kAlignThreads, (size_t)kAlignWaves * E, stream>>>(ids, P, E, counts,
+                                                                           rank);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  align_scan_kernel<<<1, kAlignThreads, 0, stream>>>(counts, C, E, P, small, big, thr, seg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  align_scatter_kernel<<<C, kAlignThreads, 0, stream>>>(ids, P, E, counts, seg, rank, small, big,
+                                                       thr);
+  return hipGetLastError();
+}
 
 size_t align_lds_bytes(int E) { return align_lds_words(E) * sizeof(int); }
 
@@ -23,17 +153,6 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
   AlignOut big{nullptr, nullptr, nullptr, 256};
   align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, small, big,
                                                                  0x7FFFFFFF, rank);
-  return hipGetLastError();
-}
-
-hipError_t launch_align_split(const int32_t* ids, int P, int E, int BM_small,
-                              int32_t* sorted_small, int32_t* bexp_small, int32_t* npp_small,
-                              int BM_big, int32_t* sorted_big, int32_t* bexp_big,
-                              int32_t* npp_big, int thr, int32_t* rank, hipStream_t stream) {
-  AlignOut small{sorted_small, bexp_small, npp_small, BM_small};
-  AlignOut big{sorted_big, bexp_big, npp_big, BM_big};
-  align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, small, big, thr,
-                                                                 rank);
   return hipGetLastError();
 }
 

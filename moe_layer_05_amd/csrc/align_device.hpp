@@ -15,11 +15,12 @@
 // counts of earlier waves plus the in-wave rank.  Every step is a pure
 // function of the input order, so the layout is deterministic and stable.
 //
-// Split form (used by the fused forward at prefill sizes): experts with at
-// least `thr` pairs are laid out in a second, separate layout padded to a
-// larger block size, for the tiled products; the others keep the small
-// blocks.  With thr beyond the pair count every expert is small and the
-// result is the plain layout above.
+// Split form: experts with at least `thr` pairs are laid out in a second,
+// separate layout padded to a larger block size, for the tiled products; the
+// others keep the small blocks.  With thr beyond the pair count every expert
+// is small and the result is the plain layout above.  (The fused forward
+// builds the split layouts for prefill with the multi-workgroup kernels of
+// align.hip, which give the same result.)
 #pragma once
 
 #include "device_common.hpp"

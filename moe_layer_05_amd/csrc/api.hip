@@ -52,7 +52,7 @@ int64_t max_blocks(int64_t P, int E, int bm) {
 constexpr int kTileThreshold = 16;
 
 struct FusedLayout {
-  size_t ids, wts, sorted, bexp, npp, rank, scal, qx, a, qa, dw, total;
+  size_t ids, wts, sorted, bexp, npp, rank, scal, qx, a, qa, dw, ascr, total;
   size_t sorted_t, bexp_t, npp_t;     // tiled layout (prefill)
   int bm;
   int64_t cap, nblk;
@@ -96,6 +96,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.bexp_t = take(L.tiled ? L.nblk_t * 4 : 0);
   L.npp_t = take(4);
   L.rank = take(P * 4);
+  L.ascr = take(L.tiled ? align_multi_workspace_bytes((int)P, E) : 0);
   L.scal = take(2 * kAmaxWords * 4);     // amax blocks of x and of a
   L.qx = take(fp8 ? (size_t)T * H : 0);
   L.a = take((size_t)P * I * (fp8 ? 4 : 2));
@@ -277,8 +278,9 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     // a2
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
     if (e == hipSuccess) {
-      e = L.tiled ? launch_align_split(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
-                                       sorted_t, bexp_t, npp_t, kTileThreshold, rank, stream)
+      e = L.tiled ? launch_align_split_multi(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
+                                             sorted_t, bexp_t, npp_t, kTileThreshold, rank,
+                                             reinterpret_cast<int32_t*>(ws + L.ascr), stream)
                   : launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
     }
   }

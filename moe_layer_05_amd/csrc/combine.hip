@@ -6,13 +6,15 @@
 // output by its routing weight and scales, so this sums, for each token, its K
 // rows over the S parts of the down product's reduction in a fixed order
 // (k = 0..K-1, then part 0..S-1: deterministic, no atomics) and rounds to
-// bfloat16 (nearest even).  8 outputs per thread: K*S x 32-byte loads, one
-// 16-byte store.
+// bfloat16 (nearest even).  8 outputs per thread: K*S x 32-byte loads (up to
+// 8 rows in flight per thread), one 16-byte store.
 #include "device_common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 namespace {
+
+constexpr int kBatch = 8;     // rows loaded per thread before they are added
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ dw, int splits,
                                                       int64_t T, int K, int H,
@@ -26,13 +28,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const float* src = dw + (t * K) * (int64_t)H + hc;
     const int64_t part = T * K * (int64_t)H;
-    for (int k = 0; k < K; ++k) {
-      for (int sp = 0; sp < splits; ++sp) {
-        const float* r = src + (int64_t)k * H + sp * part;
-        const float4 p = *reinterpret_cast<const float4*>(r);
-        const float4 q = *reinterpret_cast<const float4*>(r + 4);
-        s[0] += p.x; s[1] += p.y; s[2] += p.z; s[3] += p.w;
-        s[4] += q.x; s[5] += q.y; s[6] += q.z; s[7] += q.w;
+    const int rows = K * splits;                     // row q: k = q / splits, part q % splits
+    for (int q0 = 0; q0 < rows; q0 += kBatch) {
+      float4 p[kBatch][2];                           // all loads of a batch before the adds
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int q = q0 + b;
+        if (q < rows) {
+          const float* r = src + (int64_t)(q / splits) * H + (q % splits) * part;
+          p[b][0] = *reinterpret_cast<const float4*>(r);
+          p[b][1] = *reinterpret_cast<const float4*>(r + 4);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (q0 + b < rows) {
+          s[0] += p[b][0].x; s[1] += p[b][0].y; s[2] += p[b][0].z; s[3] += p[b][0].w;
+          s[4] += p[b][1].x; s[5] += p[b][1].y; s[6] += p[b][1].z; s[7] += p[b][1].w;
+        }
       }
     }
     uint4 o;

@@ -51,12 +51,6 @@ size_t align_lds_bytes(int E);
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream);
-// Two layouts at once: experts with >= thr pairs in blocks of BM_big, the
-// others in blocks of BM_small.
-hipError_t launch_align_split(const int32_t* ids, int P, int E, int BM_small,
-                              int32_t* sorted_small, int32_t* bexp_small, int32_t* npp_small,
-                              int BM_big, int32_t* sorted_big, int32_t* bexp_big,
-                              int32_t* npp_big, int thr, int32_t* rank, hipStream_t stream);
 
 // a1 + a0 + a2 by one workgroup for small batches (front_fits): routing,
 // (FP8) the codes of x with the final amax word, the amax slots of a cleared,
@@ -67,6 +61,16 @@ hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm
                         uint32_t* amax_a, uint8_t* qx, int BM, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream);
+
+// Two layouts at once (prefill), by three multi-workgroup launches: experts
+// with >= thr pairs in blocks of BM_big, the others in blocks of BM_small;
+// scratch holds align_multi_workspace_bytes(P, E).
+size_t align_multi_workspace_bytes(int P, int E);
+hipError_t launch_align_split_multi(const int32_t* ids, int P, int E, int BM_small,
+                                    int32_t* sorted_small, int32_t* bexp_small,
+                                    int32_t* npp_small, int BM_big, int32_t* sorted_big,
+                                    int32_t* bexp_big, int32_t* npp_big, int thr, int32_t* rank,
+                                    int32_t* scratch, hipStream_t stream);
 
 hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream);
 hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
