@@ -55,6 +55,10 @@ def parse():
                     help="no GPU run: read two rocprofv3 --pmc result folders (FETCH_SIZE, "
                          "WRITE_SIZE) of this same command with --copy-calib-mib, and store "
                          "the dominant kernel's HBM bytes per call in profiles/traffic.json")
+    ap.add_argument("--first-call-check", action="store_true",
+                    help="after the measurement, call the layer at never-seen token counts "
+                         "(1..64, 100, 257, 4096, shuffled) and compare each first call with "
+                         "the p95 of the following ten (nothing is compiled at run time)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before the layer, copy this many MiB once with a plain "
                          "device copy (a known-size reference for HBM counters)")
@@ -257,6 +261,37 @@ def oracle_and_parity(cfg, m, w, tk, budget):
     return cpu, parity
 
 
+def first_call_check(cfg, m, T_done, dev, stream):
+    """First call at each never-seen token count against the p95 of the ten
+    calls that follow it (same process, workspace sized beforehand so no call
+    allocates).  The library compiles nothing at run time, so a first call
+    costs what a later one does."""
+    import random
+    import numpy as np
+    import torch
+    from moe_layer_05_amd import workloads
+    Ts = [t for t in list(range(1, 65)) + [100, 257, 4096] if t != T_done]
+    random.Random(0).shuffle(Ts)
+    m.workspace(max(Ts), dev)
+    worst = (0.0, None)
+    for t in Ts:
+        tk = workloads.make_tokens(cfg, t, seed=1, device=dev)
+        out = torch.empty(t, cfg.H, dtype=torch.bfloat16, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(11)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            m(tk["x"], tk["logits"], out=out)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        ratio = us[0] / float(np.percentile(us[1:], 95))
+        if ratio > worst[0]:
+            worst = (ratio, t)
+    return {"t_values": len(Ts), "max_first_over_p95": round(worst[0], 3), "at_T": worst[1]}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -364,6 +399,8 @@ def main():
     roof["algorithmic_bytes"] = work.stage_bytes[dom]
     roof["algorithmic_flops"] = work.stage_flops[dom]
 
+    first_call = first_call_check(cfg, mods[0], T, dev, stream) if args.first_call_check else None
+
     cpu = parity = None
     if not args.no_cpu_baseline:
         cpu, parity = oracle_and_parity(cfg, mods[0], w, tk, args.cpu_budget)
@@ -396,6 +433,7 @@ def main():
                   "step_us_with_all_stage_events_p95": round(float(np.percentile(step_us, 95)), 2)},
         "stages_us": stage_us,
         "parity": parity,
+        "first_call": first_call,
         "source_digest": source_digest(),
     }
     print(json.dumps(line), flush=True)

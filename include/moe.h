@@ -195,8 +195,8 @@ typedef enum {
   MOE_STAGE_ALIGN = 2,        /* a2 sort of the pairs by expert              */
   MOE_STAGE_GATE_UP = 3,      /* a3+a4 gate/up product, SiLU-and-mul         */
   MOE_STAGE_INTER_QUANT = 4,  /* E4M3 quantisation of the intermediate (FP8) */
-  MOE_STAGE_DOWN = 5,         /* a5 down product, scales, routing weight     */
-  MOE_STAGE_COMBINE = 6,      /* a6 sum over the K choices, bfloat16 output  */
+  MOE_STAGE_DOWN = 5,         /* a5 down product and scales                  */
+  MOE_STAGE_COMBINE = 6,      /* a6 routing-weighted sum, bfloat16 output    */
   MOE_STAGE_COUNT = 7
 } moe_stage;
 

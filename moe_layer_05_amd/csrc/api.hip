@@ -307,7 +307,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.act_amax = fp8 ? amax_x + kAmaxFinal : nullptr;
     g.a_out = abuf;
     g.a_amax = fp8 ? amax_a : nullptr;
-    e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, stream);
+    e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, cus, stream);
     if (e == hipSuccess && L.tiled) {
       GemmParams t = g;
       t.sorted_ids = sorted_t;
@@ -337,8 +337,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.act_amax = fp8 ? amax_a + kAmaxFinal : nullptr;
     g.dw = dw;
     g.dw_split_stride = (int64_t)P * H;
-    g.topk_w = wts;
-    e = launch_gemm_decode(kDown, fp8, g, L.dn.ra, L.nblk, stream);
+    e = launch_gemm_decode(kDown, fp8, g, L.dn.ra, L.nblk, cus, stream);
     if (e == hipSuccess && L.tiled) {
       GemmParams t = g;
       t.sorted_ids = sorted_t;
@@ -352,7 +351,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   }
   // a6
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, stream);
-  if (e == hipSuccess) e = launch_combine(dw, L.dn.splits, T, K, H, a->out, cus, stream);
+  if (e == hipSuccess) e = launch_combine(dw, wts, L.dn.splits, T, K, H, a->out, cus, stream);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COUNT, stream);
   return hip_status(e);
 }

@@ -2,9 +2,9 @@
 //
 // Combining the chosen experts' outputs is part of the layer's work around the
 // matrix products (toolboxkart.tech page, "Why MoE inference needs specialized
-// kernels"); the down projection's epilogue already multiplied each pair's
-// output by its routing weight and scales, so this sums, for each token, its K
-// rows over the S parts of the down product's reduction in a fixed order
+// kernels"); the down projection's epilogue already applied the dequantisation
+// scales, so this sums, for each token, its K rows times their routing
+// weights over the S parts of the down product's reduction in a fixed order
 // (k = 0..K-1, then part 0..S-1: deterministic, no atomics) and rounds to
 // bfloat16 (nearest even).  8 outputs per thread: K*S x 32-byte loads (up to
 // 8 rows in flight per thread), one 16-byte store.
@@ -16,7 +16,8 @@ namespace {
 
 constexpr int kBatch = 8;     // rows loaded per thread before they are added
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ dw, int splits,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ dw,
+                                                      const float* __restrict__ w, int splits,
                                                       int64_t T, int K, int H,
                                                       uint4* __restrict__ out) {
   const int h8 = H / 8;
@@ -31,20 +32,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int rows = K * splits;                     // row q: k = q / splits, part q % splits
     for (int q0 = 0; q0 < rows; q0 += kBatch) {
       float4 p[kBatch][2];                           // all loads of a batch before the adds
+      float wk[kBatch];
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int q = q0 + b;
         if (q < rows) {
-          const float* r = src + (int64_t)(q / splits) * H + (q % splits) * part;
+          const int k = q / splits;
+          const float* r = src + (int64_t)k * H + (q % splits) * part;
           p[b][0] = *reinterpret_cast<const float4*>(r);
           p[b][1] = *reinterpret_cast<const float4*>(r + 4);
+          wk[b] = w[t * K + k];
         }
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         if (q0 + b < rows) {
-          s[0] += p[b][0].x; s[1] += p[b][0].y; s[2] += p[b][0].z; s[3] += p[b][0].w;
-          s[4] += p[b][1].x; s[5] += p[b][1].y; s[6] += p[b][1].z; s[7] += p[b][1].w;
+          const float c = wk[b];
+          s[0] += c * p[b][0].x; s[1] += c * p[b][0].y; s[2] += c * p[b][0].z;
+          s[3] += c * p[b][0].w; s[4] += c * p[b][1].x; s[5] += c * p[b][1].y;
+          s[6] += c * p[b][1].z; s[7] += c * p[b][1].w;
         }
       }
     }
@@ -59,13 +65,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* dw, int splits, int64_t T, int K, int H, void* out,
-                          int num_cus, hipStream_t stream) {
+hipError_t launch_combine(const float* dw, const float* w, int splits, int64_t T, int K, int H,
+                          void* out, int num_cus, hipStream_t stream) {
   const int64_t n8 = T * (int64_t)(H / 8);
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
   combine_kernel<<<(unsigned)(blocks > 0 ? blocks : 1), 256, 0, stream>>>(
-      dw, splits, T, K, H, static_cast<uint4*>(out));
+      dw, w, splits, T, K, H, static_cast<uint4*>(out));
   return hipGetLastError();
 }
 

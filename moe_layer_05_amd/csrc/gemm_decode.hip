@@ -8,9 +8,9 @@
 // page, section 1 "Swap-AB makes better use of the WGMMA tile"; kongchang.com
 // page, "Swap-AB: Making WGMMA Run at Full Utilization"; aib.vote page, second
 // paragraph: top-k=8 joins the selected experts' intermediate dimensions into
-// one large dimension).  The epilogues apply the dequantisation scales,
-// SiLU-and-mul and the routing weight in the same pass as the product
-// (aib.vote page, third paragraph).
+// one large dimension).  The epilogues apply the dequantisation scales and
+// SiLU-and-mul in the same pass as the product (aib.vote page, third
+// paragraph); the combine applies the routing weights.
 //
 // On gfx950 the row side of a 16x16 MFMA is 16 weight rows; tokens take the 16
 // columns.  Both operands are K-contiguous rows (W[row][k], X[token][k]):
@@ -36,8 +36,9 @@
 //    waves over the compute units, and units past the device-side block count
 //    leave at once (the host never reads the routing);
 //  - the down product may split its reduction dimension I into S parts; each
-//    part writes its own weighted partial rows and the combine adds the parts
+//    part writes its own partial rows and the combine adds the parts
 //    in a fixed order, so results stay deterministic.
+#include <algorithm>
 #include <cmath>
 
 #include "device_common.hpp"
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
       if (s >= nsub) continue;
       const int32_t pair = blk[s * 16 + r16];
       if (pair >= p.P) continue;
-      const float sc = scale * p.topk_w[pair];
+      const float sc = scale;
 #pragma unroll
       for (int ra = 0; ra < RA; ++ra) {
         if (!a_ok[ra]) continue;
@@ -387,6 +388,260 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
                         acc[ra][s][3] * sc);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form, for rows made of whole chunks whose parts hold at least D
+// chunks.  A wave walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...
+// (grid = the waves the chip holds at once) and its chunk stream runs across
+// unit boundaries: the next unit's first chunks load while the current one
+// finishes, so a unit costs no start-up latency.  Everything a unit needs
+// besides its rows -- its block's pair ids, its expert id and (FP8) the
+// expert's weight scale -- also arrives by direct-to-LDS loads in the same
+// ordered stream, ahead of use, into one of three small per-wave slots; no
+// register load whose wait would drain the stream sits on the path.
+//
+// Schedule, in steps t = k * cps + j (unit k, chunk j): during step t the
+// wave consumes stage t % D, then issues the chunk of step t + D into it.  At
+// the start of step t everything issued up to step t - D has landed (loads
+// complete in order; stores only add to the counter).  The ids and expert id
+// of unit k + 1 are issued while unit k's first chunk is issued (step
+// k * cps - D) and are read when unit k + 1's first chunk is issued (step
+// (k + 1) * cps - D): landed since cps >= D.  Slot k % 3 is rewritten by
+// unit k + 3's ids at step (k + 2) * cps - D, after unit k's epilogue at step
+// (k + 1) * cps - 1.
+constexpr int kMetaBytes = 768;       // pair ids [64], expert id [64], weight scale [64]
+
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(v)
+               : "v"(a)
+               : "memory");
+  return v;
+}
+
+template <int MODE, bool FP8, int NSUB, int RA, int D>
+__global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kTiles = RA + NSUB;
+  constexpr int kLoads = 4 * kTiles;
+  static_assert((D - 1) * kLoads <= 63, "ring deeper than the vmcnt counter");
+
+  const int lane = threadIdx.x;
+  const int g4 = lane >> 4;
+  const int r16 = lane & 15;
+
+  // plain loads, before the stream starts
+  const int per_block = p.groups * p.splits;
+  const int64_t total = (int64_t)(p.num_post_pad[0] / p.BM) * per_block;
+  const int64_t u0 = blockIdx.x, du = gridDim.x;
+  if (u0 >= total) return;
+  float act_scale = 1.0f;
+  if constexpr (FP8) act_scale = scale_from_amax_bits(*p.act_amax);
+
+  const int nw = (int)((total - 1 - u0) / du) + 1;         // units of this wave
+  const int row_bytes = (int)p.row_bytes;
+  const int cps = (row_bytes / kChunk) / p.splits;          // chunks per unit
+  const int nsteps = nw * cps;
+
+  uint8_t* ring = smem;
+  uint8_t* meta = smem + D * kTiles * kTileBytes;
+  const uint32_t meta_a = lds_addr(meta);
+  auto unit_pos = [&](int k, int& b, int& grp, int& split) {
+    const int64_t u = u0 + (int64_t)k * du;
+    b = (int)(u / per_block);
+    const int rem = (int)(u - (int64_t)b * per_block);
+    grp = rem % p.groups;
+    split = rem / p.groups;
+  };
+  auto meta_issue = [&](int k) {                   // ids and expert id of unit k
+    int b, grp, split;
+    unit_pos(k, b, grp, split);
+    uint8_t* slot = meta + (k % 3) * kMetaBytes;
+    const int32_t* blk = p.sorted_ids + (int64_t)b * p.BM;
+    __builtin_amdgcn_global_load_lds((const void*)(blk + (lane < p.BM ? lane : 0)),
+                                     (lds_void*)slot, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(p.block_expert + b), (lds_void*)(slot + 256),
+                                     4, 0, 0);
+  };
+
+  uint32_t pc[4];                                  // the lane's piece offset per load
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pc[i] = (uint32_t)((r16 ^ (4 * i + g4)) * 16);
+  uint32_t rd[4];                                  // MFMA-layout read addresses
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rd[j] = lds_addr(ring) + r16 * kChunk + (((4 * j + g4) ^ r16) * 16);
+
+  // ---- load side: the unit whose chunks are being issued
+  const uint8_t* src[kTiles][4];
+  int l_cbegin = 0;
+  auto load_setup = [&](int k) {                   // unit k's ids and expert id have landed
+    int b, grp, split;
+    unit_pos(k, b, grp, split);
+    const uint32_t slot = meta_a + (uint32_t)((k % 3) * kMetaBytes);
+    const int e = __builtin_amdgcn_readfirstlane((int)lds_read_u32(slot + 256));
+    const uint8_t* wexp = p.W + (int64_t)e * p.w_expert_bytes;
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra) {
+      int base;
+      if constexpr (MODE == kGateUp) {
+        const int c0 = (grp * (RA / 2) + ra / 2) * 16;
+        base = c0 < p.I ? ((ra & 1) ? p.I + c0 : c0) : 0;
+      } else {
+        const int r0 = (grp * RA + ra) * 16;
+        base = r0 < p.H ? r0 : 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) src[ra][i] = wexp + (int64_t)(base + 4 * i + g4) * row_bytes;
+    }
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = s * 16 + 4 * i + g4;
+        const int32_t pair = q < p.BM ? (int32_t)lds_read_u32(slot + 4 * q) : p.P;
+        const int64_t brow = pair < p.P ? (int64_t)(pair / p.b_row_div) : 0;
+        src[RA + s][i] = p.B + brow * row_bytes;
+      }
+    l_cbegin = split * cps;
+    if constexpr (FP8)                              // the expert's weight scale, for the epilogue
+      __builtin_amdgcn_global_load_lds((const void*)(p.w_scale + e),
+                                       (lds_void*)(meta + (k % 3) * kMetaBytes + 512), 4, 0, 0);
+  };
+  auto issue = [&](int d, int c) {
+    const uint32_t off = (uint32_t)c * kChunk;
+#pragma unroll
+    for (int t = 0; t < RA; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src[t][i] + off + pc[i]),
+            (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, kAuxNT);
+#pragma unroll
+    for (int t = RA; t < kTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src[t][i] + off + pc[i]),
+            (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, 0);
+  };
+  // issue the chunk of step t (into stage t % D), setting up its unit first
+  auto issue_step = [&](int t) {
+    const int k = t / cps, j = t - k * cps;
+    if (j == 0) {
+      load_setup(k);
+      if (k + 1 < nw) meta_issue(k + 1);
+    }
+    issue(t % D, l_cbegin + j);
+  };
+
+  // ---- compute side
+  v4f acc[RA][NSUB];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[ra][s] = v4f{0.f, 0.f, 0.f, 0.f};
+  };
+  auto consume = [&](int d) {
+    uint4 bt[NSUB][4];
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+      const uint32_t o = (uint32_t)(d * kTiles + RA + s) * kTileBytes;
+      lds_read4(bt[s], rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
+    }
+#pragma unroll
+    for (int ra = 0; ra < RA; ++ra) {
+      uint4 a[4];
+      const uint32_t o = (uint32_t)(d * kTiles + ra) * kTileBytes;
+      lds_read4(a, rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[ra][s] = Tile<FP8>::mma(a, bt[s], acc[ra][s]);
+    }
+  };
+  auto epilogue = [&](int k) {
+    int b, grp, split;
+    unit_pos(k, b, grp, split);
+    const uint32_t slot = meta_a + (uint32_t)((k % 3) * kMetaBytes);
+    float scale = 1.0f;
+    if constexpr (FP8) scale = act_scale * __uint_as_float(lds_read_u32(slot + 512));
+    if constexpr (MODE == kGateUp) {
+      float local_max = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int q = s * 16 + r16;
+        const int32_t pair = q < p.BM ? (int32_t)lds_read_u32(slot + 4 * q) : p.P;
+        if (pair >= p.P) continue;
+#pragma unroll
+        for (int cg = 0; cg < RA / 2; ++cg) {
+          const int c0 = (grp * (RA / 2) + cg) * 16;
+          if (c0 >= p.I) continue;
+          const int col = c0 + 4 * g4;
+          float av[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float gt = acc[2 * cg][s][v] * scale;
+            const float up = acc[2 * cg + 1][s][v] * scale;
+            av[v] = silu_fast(gt) * up;
+            local_max = fmaxf(local_max, fabsf(av[v]));
+          }
+          if constexpr (FP8) {
+            float* dst = static_cast<float*>(p.a_out) + (int64_t)pair * p.I + col;
+            *reinterpret_cast<float4*>(dst) = make_float4(av[0], av[1], av[2], av[3]);
+          } else {
+            uint16_t* dst = static_cast<uint16_t*>(p.a_out) + (int64_t)pair * p.I + col;
+            uint2 pk;
+            pk.x = f32_to_bf16_bits(av[0]) | (f32_to_bf16_bits(av[1]) << 16);
+            pk.y = f32_to_bf16_bits(av[2]) | (f32_to_bf16_bits(av[3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = pk;
+          }
+        }
+      }
+      if constexpr (FP8) {
+        local_max = wave_max(local_max);
+        if (lane == 0 && local_max > 0.0f)
+          amax_slot_max(p.a_amax, (uint32_t)(u0 + (int64_t)k * du), local_max);
+      }
+    } else {
+      float* part = p.dw + (int64_t)split * p.dw_split_stride;
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        const int q = s * 16 + r16;
+        const int32_t pair = q < p.BM ? (int32_t)lds_read_u32(slot + 4 * q) : p.P;
+        if (pair >= p.P) continue;
+#pragma unroll
+        for (int ra = 0; ra < RA; ++ra) {
+          const int r0 = (grp * RA + ra) * 16;
+          if (r0 >= p.H) continue;
+          float* dst = part + (int64_t)pair * p.H + r0 + 4 * g4;
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(acc[ra][s][0] * scale, acc[ra][s][1] * scale, acc[ra][s][2] * scale,
+                          acc[ra][s][3] * scale);
+        }
+      }
+    }
+  };
+
+  // ---- the stream
+  meta_issue(0);
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nsteps) issue_step(d);
+  zero_acc();
+  for (int t = 0; t < nsteps; ++t) {
+    const int later = nsteps - 1 - t;                // steps issued after this one, at most D - 1
+    if (later >= D - 1) wait_vmcnt<(D - 1) * kLoads>();
+    else wait_stages<kLoads, D>(later);
+    consume(t % D);
+    if ((t + 1) % cps == 0) {
+      epilogue(t / cps);
+      zero_acc();
+    }
+    if (t + D < nsteps) issue_step(t + D);
   }
 }
 
@@ -401,8 +656,32 @@ hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The persistent form when the rows and their parts allow it (whole chunks,
+// parts of at least D chunks) and each resident wave gets a few units (2 to
+// 7 on average: with one, the unit's ids cost an extra round trip; with many,
+// the one-wave-per-unit grid measured faster); grid = the waves resident on
+// `num_cus` units.
+template <int MODE, bool FP8, int NSUB, int RA, int D>
+hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t stream) {
+  const int64_t nchunks = p.row_bytes / kChunk;
+  const int lds = D * (RA + NSUB) * kTileBytes + 3 * kMetaBytes;
+  const int64_t resident = (int64_t)num_cus * std::max(1, (160 * 1024) / lds);
+  const bool stream_ok = p.row_bytes % kChunk == 0 && nchunks % p.splits == 0 &&
+                         nchunks / p.splits >= D && D > 1 && grid.x >= 2 * resident &&
+                         grid.x < 8 * resident;
+  if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, D>(p, grid, stream);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const unsigned g = (unsigned)std::min<int64_t>(grid.x, resident);
+  moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D><<<dim3(g), dim3(64), lds, stream>>>(p);
+  return hipGetLastError();
+}
+
 template <int MODE, bool FP8, int RA>
-hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, hipStream_t stream) {
+hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
+                       hipStream_t stream) {
   if (p.row_bytes <= kChunk) {
     // one chunk per row: no ring, so the LDS holds more waves
     switch (nsub_max) {
@@ -413,18 +692,18 @@ hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, hipStream_t
     }
   }
   switch (nsub_max) {
-    case 1: return launch_one<MODE, FP8, 1, RA, ring_depth(RA, 1)>(p, grid, stream);
-    case 2: return launch_one<MODE, FP8, 2, RA, ring_depth(RA, 2)>(p, grid, stream);
-    case 4: return launch_one<MODE, FP8, 4, RA, ring_depth(RA, 4)>(p, grid, stream);
+    case 1: return launch_best<MODE, FP8, 1, RA, ring_depth(RA, 1)>(p, grid, num_cus, stream);
+    case 2: return launch_best<MODE, FP8, 2, RA, ring_depth(RA, 2)>(p, grid, num_cus, stream);
+    case 4: return launch_best<MODE, FP8, 4, RA, ring_depth(RA, 4)>(p, grid, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int MODE, int RA>
-hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid,
+hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
                         hipStream_t stream) {
-  return fp8 ? launch_nsub<MODE, true, RA>(p, nsub_max, grid, stream)
-             : launch_nsub<MODE, false, RA>(p, nsub_max, grid, stream);
+  return fp8 ? launch_nsub<MODE, true, RA>(p, nsub_max, grid, num_cus, stream)
+             : launch_nsub<MODE, false, RA>(p, nsub_max, grid, num_cus, stream);
 }
 
 }  // namespace
@@ -492,19 +771,19 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
 }
 
 hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
-                              hipStream_t stream) {
+                              int num_cus, hipStream_t stream) {
   const int nsub_max = p.BM / 16;
   const int64_t wgs = nblk_cap * p.groups * p.splits;   // one wave each
   if (wgs <= 0) return hipSuccess;
   if (wgs > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
   if (mode == kGateUp) {
-    if (ra == 2) return launch_dtype<kGateUp, 2>(fp8, p, nsub_max, grid, stream);
-    if (ra == 4) return launch_dtype<kGateUp, 4>(fp8, p, nsub_max, grid, stream);
+    if (ra == 2) return launch_dtype<kGateUp, 2>(fp8, p, nsub_max, grid, num_cus, stream);
+    if (ra == 4) return launch_dtype<kGateUp, 4>(fp8, p, nsub_max, grid, num_cus, stream);
     return hipErrorInvalidValue;
   }
-  if (ra == 2) return launch_dtype<kDown, 2>(fp8, p, nsub_max, grid, stream);
-  if (ra == 4) return launch_dtype<kDown, 4>(fp8, p, nsub_max, grid, stream);
+  if (ra == 2) return launch_dtype<kDown, 2>(fp8, p, nsub_max, grid, num_cus, stream);
+  if (ra == 4) return launch_dtype<kDown, 4>(fp8, p, nsub_max, grid, num_cus, stream);
   return hipErrorInvalidValue;
 }
 

@@ -8,8 +8,8 @@
 // in the decode kernel (toolboxkart.tech page, section 1; aib.vote page,
 // second paragraph), so each lane's four accumulators are four consecutive
 // output features and the epilogue stores them as one vector.  The epilogues
-// apply the dequantisation scales, SiLU-and-mul, and the routing weight in the
-// same pass (aib.vote page, third paragraph).
+// apply the dequantisation scales and SiLU-and-mul in the same pass (aib.vote
+// page, third paragraph); the routing weight is applied by the combine.
 //
 // Workgroup tile: 256 weight rows x 256 tokens, 8 waves in a 2 x 4 grid, each
 // wave 128 x 64 = 8 x 4 MFMA 16x16 tiles (fp8: one 16x16x128 per tile and
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
       for (int bj = 0; bj < 4; ++bj) {
         const int32_t pair = s.blk[64 * wn + 16 * bj + l16];
         if (pair >= p.P) continue;
-        const float sc = scale * p.topk_w[pair];
+        const float sc = scale;
 #pragma unroll
         for (int ai = 0; ai < 8; ++ai) {
           const int h = s.n * kTM + 128 * wm + 16 * ai + 4 * g4;

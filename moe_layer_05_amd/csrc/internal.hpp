@@ -31,9 +31,8 @@ struct GemmParams {
   uint32_t* a_amax;            // amax block (slots) of a (FP8) or nullptr
   int I;
   // down
-  float* dw;                   // [splits][P][H] weighted expert outputs
+  float* dw;                   // [splits][P][H] scaled expert outputs
   int64_t dw_split_stride;     // elements between parts (P * H)
-  const float* topk_w;         // [P] routing weights
   int H;
 };
 
@@ -82,7 +81,7 @@ hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* 
 
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm);
 hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
-                              hipStream_t stream);
+                              int num_cus, hipStream_t stream);
 
 // Tiled products for large token blocks (BM = tile_block_m()); groups are
 // the column tiles per block.
@@ -91,7 +90,8 @@ int tile_groups(int mode, int rows);
 hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream);
 
-hipError_t launch_combine(const float* dw, int splits, int64_t T, int K, int H, void* out,
-                          int num_cus, hipStream_t stream);
+// out[t] = bf16(sum over k, then parts, of w[t*K+k] * dw[part][t*K+k])
+hipError_t launch_combine(const float* dw, const float* w, int splits, int64_t T, int K, int H,
+                          void* out, int num_cus, hipStream_t stream);
 
 }  // namespace moe
