@@ -128,7 +128,8 @@ def record_traffic(args):
                                  (args.record_traffic[1], "WRITE_SIZE", "write")):
         disp = read_counter(folder, counter)
         calib = [v for name, v in disp.values() if "bitwise_not" in name]
-        calls = sum(1 for name, _ in disp.values() if "router_kernel" in name)
+        calls = sum(1 for name, _ in disp.values()
+                    if "router_kernel" in name or "front_kernel" in name)
         stage = [v for name, v in disp.values() if STAGE_KERNELS["gate_up"].search(name)]
         if len(calib) != 1 or calls == 0 or not stage:
             raise SystemExit(f"{folder}: calibration {len(calib)}, calls {calls}, "
@@ -136,6 +137,7 @@ def record_traffic(args):
         factor = calib[0] * 1024.0 / n           # counter bytes per real byte
         rec[f"{key}_factor"] = round(factor, 4)
         rec[f"{key}_bytes_per_call"] = round(sum(stage) * 1024.0 / factor / calls)
+        rec["calls"] = calls
     rec["bytes_per_launch"] = rec["fetch_bytes_per_call"] + rec["write_bytes_per_call"]
     try:
         with open(TRAFFIC_FILE) as fh:

@@ -180,6 +180,14 @@ size_t moe_fused_workspace_bytes(const moe_fused_args* args);
 int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                           moe_wdtype wdtype);
 
+/* Enqueues the whole layer on `stream` (see the block above moe_fused_args)
+ * and returns.  The first call on a device also resolves every kernel of the
+ * library in the runtime (a one-time host cost), so no later call, at any
+ * token count, pays a kernel's first-launch lookup; nothing is compiled at
+ * run time.  Errors: MOE_ERR_NULL for a missing pointer, MOE_ERR_SHAPE /
+ * MOE_ERR_UNSUPPORTED for a shape or alignment outside the supported set,
+ * MOE_ERR_WORKSPACE when workspace_bytes is too small (all checked on the
+ * host before anything is enqueued), MOE_ERR_HIP when a launch fails. */
 moe_status moe_fused_forward(const moe_fused_args* args, hipStream_t stream);
 
 /*

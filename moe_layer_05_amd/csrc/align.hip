@@ -117,6 +117,18 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
 
 }  // namespace
 
+hipError_t prepare_align_kernels() {
+  const void* fns[] = {reinterpret_cast<const void*>(&align_kernel),
+                       reinterpret_cast<const void*>(&align_count_kernel),
+                       reinterpret_cast<const void*>(&align_scan_kernel),
+                       reinterpret_cast<const void*>(&align_scatter_kernel)};
+  for (const void* f : fns) {
+    const hipError_t e = prepare_kernel(f, 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 size_t align_multi_workspace_bytes(int P, int E) {
   const size_t C = ((size_t)P + kAlignThreads - 1) / kAlignThreads;
   return (C * E + 3 * (size_t)E) * sizeof(int32_t);

@@ -18,6 +18,29 @@ constexpr int kMaxK = 64;
 size_t round_up(size_t x) { return (x + kAlignBytes - 1) / kAlignBytes * kAlignBytes; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Every kernel of the library resolved once per device, at the first call
+// on it (so no later call, at whatever token count, pays a kernel's first
+// lookup).  Returns the first error.
+hipError_t prepare_all() {
+  static std::mutex mu;
+  static bool done[256] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 256) return hipSuccess;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev]) return hipSuccess;
+  e = prepare_decode_kernels();
+  if (e == hipSuccess) e = prepare_tile_kernels();
+  if (e == hipSuccess) e = prepare_router_kernels();
+  if (e == hipSuccess) e = prepare_align_kernels();
+  if (e == hipSuccess) e = prepare_front_kernels();
+  if (e == hipSuccess) e = prepare_quant_kernels();
+  if (e == hipSuccess) e = prepare_combine_kernels();
+  if (e == hipSuccess) done[dev] = true;
+  return e;
+}
+
 // Compute-unit count of the current device, filled once per device.
 int num_cus() {
   static std::mutex mu;
@@ -236,6 +259,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   const int H = a->H, I = a->I, E = a->E, K = a->K;
   const FusedLayout L = fused_layout(T, H, I, E, K, a->wdtype);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
 
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   int32_t* ids = a->topk_ids_out ? a->topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);

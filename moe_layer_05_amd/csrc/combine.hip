@@ -65,6 +65,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
+hipError_t prepare_combine_kernels() {
+  return prepare_kernel(reinterpret_cast<const void*>(&combine_kernel), 0);
+}
+
 hipError_t launch_combine(const float* dw, const float* w, int splits, int64_t T, int K, int H,
                           void* out, int num_cus, hipStream_t stream) {
   const int64_t n8 = T * (int64_t)(H / 8);

@@ -120,6 +120,25 @@ hipError_t launch_vpl(const FrontArgs& a, int vpl, size_t lds, hipStream_t strea
 
 }  // namespace
 
+hipError_t prepare_front_kernels() {
+  const void* fns[] = {
+      reinterpret_cast<const void*>(&front_kernel<1, false>),
+      reinterpret_cast<const void*>(&front_kernel<2, false>),
+      reinterpret_cast<const void*>(&front_kernel<4, false>),
+      reinterpret_cast<const void*>(&front_kernel<8, false>),
+      reinterpret_cast<const void*>(&front_kernel<16, false>),
+      reinterpret_cast<const void*>(&front_kernel<1, true>),
+      reinterpret_cast<const void*>(&front_kernel<2, true>),
+      reinterpret_cast<const void*>(&front_kernel<4, true>),
+      reinterpret_cast<const void*>(&front_kernel<8, true>),
+      reinterpret_cast<const void*>(&front_kernel<16, true>)};
+  for (const void* f : fns) {
+    const hipError_t e = prepare_kernel(f, 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 bool front_fits(int64_t T, int H, int K, bool fp8) {
   // one wave per token, the pairs in one align chunk, and (FP8) x small
   // enough for every quantising workgroup to read all of it

@@ -646,11 +646,25 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
 }
 
 template <int MODE, bool FP8, int NSUB, int RA, int D>
+hipError_t ready_one() {
+  static const hipError_t attr =
+      prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D>),
+                     D * (RA + NSUB) * kTileBytes);
+  return attr;
+}
+
+template <int MODE, bool FP8, int NSUB, int RA, int D>
+hipError_t ready_stream() {
+  static const hipError_t attr =
+      prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
+                     D * (RA + NSUB) * kTileBytes + 3 * kMetaBytes);
+  return attr;
+}
+
+template <int MODE, bool FP8, int NSUB, int RA, int D>
 hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
   const int lds = D * (RA + NSUB) * kTileBytes;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const hipError_t attr = ready_one<MODE, FP8, NSUB, RA, D>();
   if (attr != hipSuccess) return attr;
   moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D><<<grid, dim3(64), lds, stream>>>(p);
   return hipGetLastError();
@@ -670,9 +684,7 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
                          nchunks / p.splits >= D && D > 1 && grid.x >= 2 * resident &&
                          grid.x < 8 * resident;
   if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, D>(p, grid, stream);
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  const hipError_t attr = ready_stream<MODE, FP8, NSUB, RA, D>();
   if (attr != hipSuccess) return attr;
   const unsigned g = (unsigned)std::min<int64_t>(grid.x, resident);
   moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D><<<dim3(g), dim3(64), lds, stream>>>(p);
@@ -706,7 +718,35 @@ hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid, 
              : launch_nsub<MODE, false, RA>(p, nsub_max, grid, num_cus, stream);
 }
 
+template <int MODE, bool FP8, int RA, int NSUB>
+hipError_t ready_shape() {
+  hipError_t e = ready_one<MODE, FP8, NSUB, RA, 1>();
+  if (e == hipSuccess) e = ready_one<MODE, FP8, NSUB, RA, ring_depth(RA, NSUB)>();
+  if (e == hipSuccess) e = ready_stream<MODE, FP8, NSUB, RA, ring_depth(RA, NSUB)>();
+  return e;
+}
+
+template <int MODE, bool FP8, int RA>
+hipError_t ready_ra() {
+  hipError_t e = ready_shape<MODE, FP8, RA, 1>();
+  if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 2>();
+  if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 4>();
+  return e;
+}
+
 }  // namespace
+
+hipError_t prepare_decode_kernels() {
+  hipError_t e = ready_ra<kGateUp, false, 2>();
+  if (e == hipSuccess) e = ready_ra<kGateUp, false, 4>();
+  if (e == hipSuccess) e = ready_ra<kGateUp, true, 2>();
+  if (e == hipSuccess) e = ready_ra<kGateUp, true, 4>();
+  if (e == hipSuccess) e = ready_ra<kDown, false, 2>();
+  if (e == hipSuccess) e = ready_ra<kDown, false, 4>();
+  if (e == hipSuccess) e = ready_ra<kDown, true, 2>();
+  if (e == hipSuccess) e = ready_ra<kDown, true, 4>();
+  return e;
+}
 
 namespace {
 

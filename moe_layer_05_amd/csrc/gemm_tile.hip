@@ -339,16 +339,29 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
 }
 
 template <int MODE, bool FP8>
+hipError_t ready_tile() {
+  static const hipError_t attr =
+      prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FP8>), kTileLds);
+  return attr;
+}
+
+template <int MODE, bool FP8>
 hipError_t launch_tile(const GemmParams& p, dim3 grid, hipStream_t stream) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FP8>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kTileLds);
+  const hipError_t attr = ready_tile<MODE, FP8>();
   if (attr != hipSuccess) return attr;
   moe_gemm_tile_kernel<MODE, FP8><<<grid, dim3(64 * kWaves), kTileLds, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t prepare_tile_kernels() {
+  hipError_t e = ready_tile<kGateUp, false>();
+  if (e == hipSuccess) e = ready_tile<kGateUp, true>();
+  if (e == hipSuccess) e = ready_tile<kDown, false>();
+  if (e == hipSuccess) e = ready_tile<kDown, true>();
+  return e;
+}
 
 int tile_block_m() { return kTN; }
 

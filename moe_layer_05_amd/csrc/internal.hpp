@@ -79,6 +79,23 @@ hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* 
 hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream);
 
+// Resolve a kernel in the runtime ahead of its first launch (with the dynamic
+// LDS limit it needs when lds > 0): the first launch of a kernel otherwise
+// pays the runtime's lookup, which a first call at a new token count would
+// show.  Each file prepares every kernel it may launch.
+inline hipError_t prepare_kernel(const void* fn, int lds) {
+  if (lds > 0) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipFuncAttributes attr;
+  return hipFuncGetAttributes(&attr, fn);
+}
+hipError_t prepare_decode_kernels();
+hipError_t prepare_tile_kernels();
+hipError_t prepare_router_kernels();
+hipError_t prepare_align_kernels();
+hipError_t prepare_front_kernels();
+hipError_t prepare_quant_kernels();
+hipError_t prepare_combine_kernels();
+
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm);
 hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
                               int num_cus, hipStream_t stream);

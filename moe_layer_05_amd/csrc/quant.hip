@@ -86,6 +86,18 @@ unsigned stream_grid(int64_t n8, int num_cus) {
 
 }  // namespace
 
+hipError_t prepare_quant_kernels() {
+  const void* fns[] = {reinterpret_cast<const void*>(&amax_bf16_kernel),
+                       reinterpret_cast<const void*>(&quant_bf16_kernel),
+                       reinterpret_cast<const void*>(&quant_f32_kernel),
+                       reinterpret_cast<const void*>(&zero_amax_kernel)};
+  for (const void* f : fns) {
+    const hipError_t e = prepare_kernel(f, 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream) {
   zero_amax_kernel<<<1, 64, 0, stream>>>(p, nblocks);
   return hipGetLastError();

@@ -21,6 +21,19 @@ __global__ __launch_bounds__(256) void router_kernel(
 
 }  // namespace
 
+hipError_t prepare_router_kernels() {
+  const void* fns[] = {reinterpret_cast<const void*>(&router_kernel<1>),
+                       reinterpret_cast<const void*>(&router_kernel<2>),
+                       reinterpret_cast<const void*>(&router_kernel<4>),
+                       reinterpret_cast<const void*>(&router_kernel<8>),
+                       reinterpret_cast<const void*>(&router_kernel<16>)};
+  for (const void* f : fns) {
+    const hipError_t e = prepare_kernel(f, 0);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renorm,
                          int32_t* ids, float* wts, uint32_t* zero_amax,
                          int n_amax, hipStream_t stream) {
