@@ -392,26 +392,30 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent form, for rows made of whole chunks whose parts hold at least D
-// chunks.  A wave walks units u = blockIdx.x, blockIdx.x + gridDim.x, ...
-// (grid = the waves the chip holds at once) and its chunk stream runs across
-// unit boundaries: the next unit's first chunks load while the current one
-// finishes, so a unit costs no start-up latency.  Everything a unit needs
+// Persistent form.  A wave walks units u = blockIdx.x, blockIdx.x + gridDim.x,
+// ... (grid = the waves the chip holds at once) and its chunk stream runs
+// across unit boundaries: the next units' first chunks load while the current
+// one finishes, so a unit costs no start-up latency.  Everything a unit needs
 // besides its rows -- its block's pair ids, its expert id and (FP8) the
 // expert's weight scale -- also arrives by direct-to-LDS loads in the same
-// ordered stream, ahead of use, into one of three small per-wave slots; no
-// register load whose wait would drain the stream sits on the path.
+// ordered stream, ahead of use, into small per-wave slots; no register load
+// whose wait would drain the stream sits on the path.  Rows may end in a
+// partial chunk (as in the one-wave-per-unit form).
 //
-// Schedule, in steps t = k * cps + j (unit k, chunk j): during step t the
-// wave consumes stage t % D, then issues the chunk of step t + D into it.  At
-// the start of step t everything issued up to step t - D has landed (loads
-// complete in order; stores only add to the counter).  The ids and expert id
-// of unit k + 1 are issued while unit k's first chunk is issued (step
-// k * cps - D) and are read when unit k + 1's first chunk is issued (step
-// (k + 1) * cps - D): landed since cps >= D.  Slot k % 3 is rewritten by
-// unit k + 3's ids at step (k + 2) * cps - D, after unit k's epilogue at step
-// (k + 1) * cps - 1.
-constexpr int kMetaBytes = 768;       // pair ids [64], expert id [64], weight scale [64]
+// Schedule, in steps t = k * cps + j (unit k, chunk j, cps chunks per unit):
+// during step t the wave consumes stage t % D, then issues the chunk of step
+// t + D into it.  At the start of step t everything issued during steps up to
+// t - D has landed (loads complete in order; stores only add to the counter).
+// The chunks of unit k start to be issued at step k * cps - D, which reads
+// unit k's ids and expert id and issues those of unit k + m, m = ceil(D / cps):
+// issued at step (k - m) * cps - D <= k * cps - 2 D, they have landed.  With
+// NS = 2 m + 1 slots, unit k + NS's ids overwrite slot k at step
+// (k + m + 1) * cps - D, after unit k's epilogue at step (k + 1) * cps - 1.
+constexpr int kMetaBytes = 272;       // pair ids [64], expert id, weight scale (16-byte slots)
+
+// Units whose ids are issued ahead, and slots, for cps chunks per unit.
+__host__ __device__ constexpr int meta_ahead(int d, int cps) { return (d + cps - 1) / cps; }
+__host__ __device__ constexpr int meta_slots(int d, int cps) { return 2 * meta_ahead(d, cps) + 1; }
 
 __device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
   uint32_t v;
@@ -444,8 +448,11 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
 
   const int nw = (int)((total - 1 - u0) / du) + 1;         // units of this wave
   const int row_bytes = (int)p.row_bytes;
-  const int cps = (row_bytes / kChunk) / p.splits;          // chunks per unit
+  const int nchunks = (row_bytes + kChunk - 1) / kChunk;
+  const bool part_tail = row_bytes % kChunk != 0;           // the last chunk is partial
+  const int cps = nchunks / p.splits;                       // chunks per unit
   const int nsteps = nw * cps;
+  const int ahead = meta_ahead(D, cps), nslots = meta_slots(D, cps);
 
   uint8_t* ring = smem;
   uint8_t* meta = smem + D * kTiles * kTileBytes;
@@ -460,12 +467,13 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
   auto meta_issue = [&](int k) {                   // ids and expert id of unit k
     int b, grp, split;
     unit_pos(k, b, grp, split);
-    uint8_t* slot = meta + (k % 3) * kMetaBytes;
+    uint8_t* slot = meta + (k % nslots) * kMetaBytes;
     const int32_t* blk = p.sorted_ids + (int64_t)b * p.BM;
     __builtin_amdgcn_global_load_lds((const void*)(blk + (lane < p.BM ? lane : 0)),
                                      (lds_void*)slot, 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(p.block_expert + b), (lds_void*)(slot + 256),
-                                     4, 0, 0);
+    if (lane == 0)                                 // one word: lane 0 writes at the slot base
+      __builtin_amdgcn_global_load_lds((const void*)(p.block_expert + b),
+                                       (lds_void*)(slot + 256), 4, 0, 0);
   };
 
   uint32_t pc[4];                                  // the lane's piece offset per load
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
   auto load_setup = [&](int k) {                   // unit k's ids and expert id have landed
     int b, grp, split;
     unit_pos(k, b, grp, split);
-    const uint32_t slot = meta_a + (uint32_t)((k % 3) * kMetaBytes);
+    const uint32_t slot = meta_a + (uint32_t)((k % nslots) * kMetaBytes);
     const int e = __builtin_amdgcn_readfirstlane((int)lds_read_u32(slot + 256));
     const uint8_t* wexp = p.W + (int64_t)e * p.w_expert_bytes;
 #pragma unroll
@@ -507,25 +515,34 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
         src[RA + s][i] = p.B + brow * row_bytes;
       }
     l_cbegin = split * cps;
-    if constexpr (FP8)                              // the expert's weight scale, for the epilogue
-      __builtin_amdgcn_global_load_lds((const void*)(p.w_scale + e),
-                                       (lds_void*)(meta + (k % 3) * kMetaBytes + 512), 4, 0, 0);
+    if constexpr (FP8) {                            // the expert's weight scale, for the epilogue
+      if (lane == 0)
+        __builtin_amdgcn_global_load_lds((const void*)(p.w_scale + e),
+                                         (lds_void*)(meta + (k % nslots) * kMetaBytes + 260), 4,
+                                         0, 0);
+    }
   };
+  // pieces past the row end (partial last chunk) are read from the row start
+  // (valid memory) and zeroed on the token side after the read
   auto issue = [&](int d, int c) {
     const uint32_t off = (uint32_t)c * kChunk;
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (off + pc[i] < (uint32_t)row_bytes) ? off + pc[i] : 0u;
 #pragma unroll
     for (int t = 0; t < RA; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_global_load_lds(
-            (const void*)(src[t][i] + off + pc[i]),
+            (const void*)(src[t][i] + o[i]),
             (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, kAuxNT);
 #pragma unroll
     for (int t = RA; t < kTiles; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_global_load_lds(
-            (const void*)(src[t][i] + off + pc[i]),
+            (const void*)(src[t][i] + o[i]),
             (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, 0);
   };
   // issue the chunk of step t (into stage t % D), setting up its unit first
@@ -533,7 +550,7 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
     const int k = t / cps, j = t - k * cps;
     if (j == 0) {
       load_setup(k);
-      if (k + 1 < nw) meta_issue(k + 1);
+      if (k + ahead < nw) meta_issue(k + ahead);
     }
     issue(t % D, l_cbegin + j);
   };
@@ -546,12 +563,17 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) acc[ra][s] = v4f{0.f, 0.f, 0.f, 0.f};
   };
-  auto consume = [&](int d) {
+  auto consume = [&](int d, bool tail, uint32_t off) {
     uint4 bt[NSUB][4];
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       const uint32_t o = (uint32_t)(d * kTiles + RA + s) * kTileBytes;
       lds_read4(bt[s], rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
+      if (tail) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (off + (4 * j + g4) * 16 >= (uint32_t)row_bytes) bt[s][j] = make_uint4(0, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int ra = 0; ra < RA; ++ra) {
@@ -565,9 +587,9 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
   auto epilogue = [&](int k) {
     int b, grp, split;
     unit_pos(k, b, grp, split);
-    const uint32_t slot = meta_a + (uint32_t)((k % 3) * kMetaBytes);
+    const uint32_t slot = meta_a + (uint32_t)((k % nslots) * kMetaBytes);
     float scale = 1.0f;
-    if constexpr (FP8) scale = act_scale * __uint_as_float(lds_read_u32(slot + 512));
+    if constexpr (FP8) scale = act_scale * __uint_as_float(lds_read_u32(slot + 260));
     if constexpr (MODE == kGateUp) {
       float local_max = 0.0f;
 #pragma unroll
@@ -626,7 +648,7 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
   };
 
   // ---- the stream
-  meta_issue(0);
+  for (int k = 0; k < ahead && k < nw; ++k) meta_issue(k);
   wait_vmcnt<0>();
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -636,7 +658,11 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
     const int later = nsteps - 1 - t;                // steps issued after this one, at most D - 1
     if (later >= D - 1) wait_vmcnt<(D - 1) * kLoads>();
     else wait_stages<kLoads, D>(later);
-    consume(t % D);
+    const int j = t % cps;
+    const bool tail = part_tail && j == cps - 1 &&
+                      (int)((u0 + (int64_t)(t / cps) * du) % per_block) / p.groups ==
+                          p.splits - 1;
+    consume(t % D, tail, (uint32_t)(nchunks - 1) * kChunk);
     if ((t + 1) % cps == 0) {
       epilogue(t / cps);
       zero_acc();
@@ -653,11 +679,16 @@ hipError_t ready_one() {
   return attr;
 }
 
+// LDS of the stream form: the ring and the id slots for cps chunks per unit.
+constexpr int stream_lds(int d, int tiles, int cps) {
+  return d * tiles * kTileBytes + meta_slots(d, cps) * kMetaBytes;
+}
+
 template <int MODE, bool FP8, int NSUB, int RA, int D>
-hipError_t ready_stream() {
+hipError_t ready_stream() {                        // the limit for the most slots (cps = 1)
   static const hipError_t attr =
       prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
-                     D * (RA + NSUB) * kTileBytes + 3 * kMetaBytes);
+                     stream_lds(D, RA + NSUB, 1));
   return attr;
 }
 
@@ -670,24 +701,24 @@ hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The persistent form when the rows and their parts allow it (whole chunks,
-// parts of at least D chunks) and each resident wave gets a few units (2 to
-// 7 on average: with one, the unit's ids cost an extra round trip; with many,
-// the one-wave-per-unit grid measured faster); grid = the waves resident on
-// `num_cus` units.
-template <int MODE, bool FP8, int NSUB, int RA, int D>
+// The persistent form (ring depth DS) when each resident wave gets 2 to 7
+// units on average (with one unit the unit's ids cost an extra round trip;
+// with many units, and for one-chunk rows, the one-wave-per-unit grid with
+// ring depth DC measured faster); the parts of the reduction must be equal.
+// Grid = the waves resident on `num_cus` compute units.
+template <int MODE, bool FP8, int NSUB, int RA, int DC, int DS>
 hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t stream) {
-  const int64_t nchunks = p.row_bytes / kChunk;
-  const int lds = D * (RA + NSUB) * kTileBytes + 3 * kMetaBytes;
+  const int64_t nchunks = (p.row_bytes + kChunk - 1) / kChunk;
+  const int cps = (int)(nchunks / p.splits);
+  const int lds = stream_lds(DS, RA + NSUB, cps > 0 ? cps : 1);
   const int64_t resident = (int64_t)num_cus * std::max(1, (160 * 1024) / lds);
-  const bool stream_ok = p.row_bytes % kChunk == 0 && nchunks % p.splits == 0 &&
-                         nchunks / p.splits >= D && D > 1 && grid.x >= 2 * resident &&
-                         grid.x < 8 * resident;
-  if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, D>(p, grid, stream);
-  const hipError_t attr = ready_stream<MODE, FP8, NSUB, RA, D>();
+  const bool stream_ok = DS > 1 && nchunks % p.splits == 0 && cps >= 1 &&
+                         grid.x >= 2 * resident && grid.x < 8 * resident;
+  if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, DC>(p, grid, stream);
+  const hipError_t attr = ready_stream<MODE, FP8, NSUB, RA, DS>();
   if (attr != hipSuccess) return attr;
   const unsigned g = (unsigned)std::min<int64_t>(grid.x, resident);
-  moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D><<<dim3(g), dim3(64), lds, stream>>>(p);
+  moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, DS><<<dim3(g), dim3(64), lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -695,18 +726,22 @@ template <int MODE, bool FP8, int RA>
 hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
                        hipStream_t stream) {
   if (p.row_bytes <= kChunk) {
-    // one chunk per row: no ring, so the LDS holds more waves
+    // one chunk per row: the one-wave-per-unit form needs no ring, so the LDS
+    // holds more waves; the stream form keeps its ring across units
     switch (nsub_max) {
-      case 1: return launch_one<MODE, FP8, 1, RA, 1>(p, grid, stream);
-      case 2: return launch_one<MODE, FP8, 2, RA, 1>(p, grid, stream);
-      case 4: return launch_one<MODE, FP8, 4, RA, 1>(p, grid, stream);
+      case 1: return launch_best<MODE, FP8, 1, RA, 1, ring_depth(RA, 1)>(p, grid, num_cus, stream);
+      case 2: return launch_best<MODE, FP8, 2, RA, 1, ring_depth(RA, 2)>(p, grid, num_cus, stream);
+      case 4: return launch_best<MODE, FP8, 4, RA, 1, ring_depth(RA, 4)>(p, grid, num_cus, stream);
       default: return hipErrorInvalidValue;
     }
   }
   switch (nsub_max) {
-    case 1: return launch_best<MODE, FP8, 1, RA, ring_depth(RA, 1)>(p, grid, num_cus, stream);
-    case 2: return launch_best<MODE, FP8, 2, RA, ring_depth(RA, 2)>(p, grid, num_cus, stream);
-    case 4: return launch_best<MODE, FP8, 4, RA, ring_depth(RA, 4)>(p, grid, num_cus, stream);
+    case 1: return launch_best<MODE, FP8, 1, RA, ring_depth(RA, 1), ring_depth(RA, 1)>(
+        p, grid, num_cus, stream);
+    case 2: return launch_best<MODE, FP8, 2, RA, ring_depth(RA, 2), ring_depth(RA, 2)>(
+        p, grid, num_cus, stream);
+    case 4: return launch_best<MODE, FP8, 4, RA, ring_depth(RA, 4), ring_depth(RA, 4)>(
+        p, grid, num_cus, stream);
     default: return hipErrorInvalidValue;
   }
 }
