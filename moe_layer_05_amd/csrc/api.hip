@@ -221,7 +221,7 @@ int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
   // sized for a few times that mean (blocks up to 64 tokens).
   if (T <= 16) return 16;
   const int64_t mean = (E > 0) ? (T * (int64_t)K + E - 1) / E : T;
-  if (mean <= 4) return 16;
+  if (mean <= 8) return 16;
   if (T <= 32 || mean <= 16) return 32;
   return 64;
 }

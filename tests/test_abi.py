@@ -151,6 +151,7 @@ def test_fused_block_m_and_workspace(L):
     assert all(b in (16, 32, 64, 128, 256) for b in bm)
     assert bm[:3] == [16, 16, 16]                    # T <= 16: one 16-token block
     assert bm[5] == 16                               # 2 tokens per expert on average
+    assert L.moe_fused_block_m(32, 4096, 14336, 8, 2, 0) == 16     # 8 per expert
     assert L.moe_fused_block_m(64, 4096, 14336, 8, 2, 0) == 32     # 16 per expert
     assert L.moe_fused_block_m(256, 4096, 192, 128, 8, 1) == 32    # 16 per expert
     assert L.moe_fused_block_m(4096, 7168, 2048, 256, 8, 1) == 64  # 128 per expert
