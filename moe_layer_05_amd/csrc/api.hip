@@ -124,7 +124,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.qx = take(fp8 ? (size_t)T * H : 0);
   L.a = take((size_t)P * I * (fp8 ? 4 : 2));
   L.qa = take(fp8 ? (size_t)P * I : 0);
-  L.dw = take((size_t)L.dn.splits * P * H * 4);
+  L.dw = take((size_t)L.dn.splits * P * H * (L.tiled ? 2 : 4));   // bfloat16 at prefill
   L.total = off;
   return L;
 }
@@ -273,7 +273,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   uint8_t* qx = ws + L.qx;
   void* abuf = ws + L.a;
   uint8_t* qa = ws + L.qa;
-  float* dw = reinterpret_cast<float*>(ws + L.dw);
+  void* dw = ws + L.dw;
   const int P = (int)(T * K);
   const int cus = num_cus();
   const int welem = fp8 ? 1 : 2;
@@ -361,6 +361,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.act_amax = fp8 ? amax_a + kAmaxFinal : nullptr;
     g.dw = dw;
     g.dw_split_stride = (int64_t)P * H;
+    g.dw_bf16 = L.tiled ? 1 : 0;
     e = launch_gemm_decode(kDown, fp8, g, L.dn.ra, L.nblk, cus, stream);
     if (e == hipSuccess && L.tiled) {
       GemmParams t = g;
@@ -375,7 +376,8 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   }
   // a6
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, stream);
-  if (e == hipSuccess) e = launch_combine(dw, wts, L.dn.splits, T, K, H, a->out, cus, stream);
+  if (e == hipSuccess)
+    e = launch_combine(dw, L.tiled, wts, L.dn.splits, T, K, H, a->out, cus, stream);
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_COUNT, stream);
   return hip_status(e);
 }

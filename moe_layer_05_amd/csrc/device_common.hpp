@@ -25,6 +25,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Four consecutive partial outputs at element `idx` of a partial-row buffer:
+// float32, or bfloat16 (nearest even) when `bf16`.
+__device__ __forceinline__ void store_part4(void* buf, bool bf16, int64_t idx, float a, float b,
+                                            float c, float d) {
+  if (bf16) {
+    uint2 pk;
+    pk.x = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    pk.y = f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(buf) + idx) = pk;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(buf) + idx) = make_float4(a, b, c, d);
+  }
+}
+
 // ---------------------------------------------------------------- E4M3
 
 // float32 -> OCP E4M3 code: nearest, ties to the even mantissa, saturating to

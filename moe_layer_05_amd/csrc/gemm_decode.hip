@@ -372,7 +372,7 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
       if (lane == 0 && local_max > 0.0f) amax_slot_max(p.a_amax, (uint32_t)unit, local_max);
     }
   } else {
-    float* part = p.dw + (int64_t)split * p.dw_split_stride;
+    const int64_t part = (int64_t)split * p.dw_split_stride;
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
       if (s >= nsub) continue;
@@ -382,10 +382,9 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
 #pragma unroll
       for (int ra = 0; ra < RA; ++ra) {
         if (!a_ok[ra]) continue;
-        float* dst = part + (int64_t)pair * p.H + row0[ra] + 4 * g4;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(acc[ra][s][0] * sc, acc[ra][s][1] * sc, acc[ra][s][2] * sc,
-                        acc[ra][s][3] * sc);
+        store_part4(p.dw, p.dw_bf16, part + (int64_t)pair * p.H + row0[ra] + 4 * g4,
+                    acc[ra][s][0] * sc, acc[ra][s][1] * sc, acc[ra][s][2] * sc,
+                    acc[ra][s][3] * sc);
       }
     }
   }
@@ -628,7 +627,7 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
           amax_slot_max(p.a_amax, (uint32_t)(u0 + (int64_t)k * du), local_max);
       }
     } else {
-      float* part = p.dw + (int64_t)split * p.dw_split_stride;
+      const int64_t part = (int64_t)split * p.dw_split_stride;
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) {
         const int q = s * 16 + r16;
@@ -638,10 +637,9 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
         for (int ra = 0; ra < RA; ++ra) {
           const int r0 = (grp * RA + ra) * 16;
           if (r0 >= p.H) continue;
-          float* dst = part + (int64_t)pair * p.H + r0 + 4 * g4;
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(acc[ra][s][0] * scale, acc[ra][s][1] * scale, acc[ra][s][2] * scale,
-                          acc[ra][s][3] * scale);
+          store_part4(p.dw, p.dw_bf16, part + (int64_t)pair * p.H + r0 + 4 * g4,
+                      acc[ra][s][0] * scale, acc[ra][s][1] * scale, acc[ra][s][2] * scale,
+                      acc[ra][s][3] * scale);
         }
       }
     }

@@ -297,10 +297,8 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
         for (int ai = 0; ai < 8; ++ai) {
           const int h = s.n * kTM + 128 * wm + 16 * ai + 4 * g4;
           if (h >= p.H) continue;
-          float* dst = p.dw + (int64_t)pair * p.H + h;
-          *reinterpret_cast<float4*>(dst) =
-              make_float4(acc[ai][bj][0] * sc, acc[ai][bj][1] * sc, acc[ai][bj][2] * sc,
-                          acc[ai][bj][3] * sc);
+          store_part4(p.dw, p.dw_bf16, (int64_t)pair * p.H + h, acc[ai][bj][0] * sc,
+                      acc[ai][bj][1] * sc, acc[ai][bj][2] * sc, acc[ai][bj][3] * sc);
         }
       }
     }

@@ -31,8 +31,9 @@ struct GemmParams {
   uint32_t* a_amax;            // amax block (slots) of a (FP8) or nullptr
   int I;
   // down
-  float* dw;                   // [splits][P][H] scaled expert outputs
+  void* dw;                    // [splits][P][H] scaled expert outputs, float32 or bfloat16
   int64_t dw_split_stride;     // elements between parts (P * H)
+  int dw_bf16;                 // the partial rows are bfloat16 (prefill) instead of float32
   int H;
 };
 
@@ -107,8 +108,9 @@ int tile_groups(int mode, int rows);
 hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream);
 
-// out[t] = bf16(sum over k, then parts, of w[t*K+k] * dw[part][t*K+k])
-hipError_t launch_combine(const float* dw, const float* w, int splits, int64_t T, int K, int H,
-                          void* out, int num_cus, hipStream_t stream);
+// out[t] = bf16(sum over k, then parts, of w[t*K+k] * dw[part][t*K+k]); dw
+// float32, or bfloat16 when dw_bf16
+hipError_t launch_combine(const void* dw, bool dw_bf16, const float* w, int splits, int64_t T,
+                          int K, int H, void* out, int num_cus, hipStream_t stream);
 
 }  // namespace moe
