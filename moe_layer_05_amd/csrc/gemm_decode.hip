@@ -103,8 +103,9 @@ __device__ __forceinline__ void wait_stages(int stages) {
 // a compute unit keep the most weight bytes in flight (waves per unit x
 // (D - 1) x RA x 4 KB), within the 6-bit vector-memory counter.
 constexpr int ring_depth(int ra, int nsub) {
-  return nsub == 1 ? (ra == 1 ? 5 : (ra == 2 ? 4 : 3))
-                   : (nsub == 2 ? (ra == 4 ? 3 : (ra == 2 ? 3 : 4)) : 2);
+  return ra >= 8 ? 2
+                 : nsub == 1 ? (ra == 1 ? 5 : (ra == 2 ? 4 : 3))
+                             : (nsub == 2 ? (ra == 4 ? 3 : (ra == 2 ? 3 : 4)) : 2);
 }
 
 template <bool FP8>
@@ -723,13 +724,19 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
 template <int MODE, bool FP8, int RA>
 hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
                        hipStream_t stream) {
+  if constexpr (RA >= 8) {
+    if (nsub_max > 2) return hipErrorInvalidValue;   // would not fit the registers
+  }
   if (p.row_bytes <= kChunk) {
     // one chunk per row: the one-wave-per-unit form needs no ring, so the LDS
     // holds more waves; the stream form keeps its ring across units
     switch (nsub_max) {
       case 1: return launch_best<MODE, FP8, 1, RA, 1, ring_depth(RA, 1)>(p, grid, num_cus, stream);
       case 2: return launch_best<MODE, FP8, 2, RA, 1, ring_depth(RA, 2)>(p, grid, num_cus, stream);
-      case 4: return launch_best<MODE, FP8, 4, RA, 1, ring_depth(RA, 4)>(p, grid, num_cus, stream);
+      case 4:
+        if constexpr (RA < 8)
+          return launch_best<MODE, FP8, 4, RA, 1, ring_depth(RA, 4)>(p, grid, num_cus, stream);
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
@@ -738,8 +745,11 @@ hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus
         p, grid, num_cus, stream);
     case 2: return launch_best<MODE, FP8, 2, RA, ring_depth(RA, 2), ring_depth(RA, 2)>(
         p, grid, num_cus, stream);
-    case 4: return launch_best<MODE, FP8, 4, RA, ring_depth(RA, 4), ring_depth(RA, 4)>(
-        p, grid, num_cus, stream);
+    case 4:
+      if constexpr (RA < 8)
+        return launch_best<MODE, FP8, 4, RA, ring_depth(RA, 4), ring_depth(RA, 4)>(
+            p, grid, num_cus, stream);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -763,7 +773,8 @@ template <int MODE, bool FP8, int RA>
 hipError_t ready_ra() {
   hipError_t e = ready_shape<MODE, FP8, RA, 1>();
   if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 2>();
-  if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 4>();
+  if constexpr (RA < 8)                            // RA = 8 takes at most 2 token tiles
+    if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 4>();
   return e;
 }
 
@@ -778,6 +789,8 @@ hipError_t prepare_decode_kernels() {
   if (e == hipSuccess) e = ready_ra<kDown, false, 4>();
   if (e == hipSuccess) e = ready_ra<kDown, true, 2>();
   if (e == hipSuccess) e = ready_ra<kDown, true, 4>();
+  if (e == hipSuccess) e = ready_ra<kDown, false, 8>();
+  if (e == hipSuccess) e = ready_ra<kDown, true, 8>();
   return e;
 }
 
@@ -836,7 +849,11 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
     auto units = [&](int ra) {
       return nblk_cap * ((rows + 16 * ra - 1) / (16 * ra)) * splits_of(ra);
     };
-    s.ra = row_bytes < 512 ? 4 : pick(nsub == 1 ? 2 : 4, units);
+    // one-chunk rows: 8 weight tiles per wave with 2 token tiles (measured
+    // on the TP8 slice: T = 256 down 48.8 -> 42.1 us; with 1 token tile 4
+    // tiles stay faster)
+    s.ra = row_bytes <= kChunk ? (nsub == 2 ? 8 : 4)
+                               : row_bytes < 512 ? 4 : pick(nsub == 1 ? 2 : 4, units);
     s.groups = (rows + 16 * s.ra - 1) / (16 * s.ra);
     s.splits = splits_of(s.ra);
   }
@@ -857,6 +874,7 @@ hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, i
   }
   if (ra == 2) return launch_dtype<kDown, 2>(fp8, p, nsub_max, grid, num_cus, stream);
   if (ra == 4) return launch_dtype<kDown, 4>(fp8, p, nsub_max, grid, num_cus, stream);
+  if (ra == 8) return launch_dtype<kDown, 8>(fp8, p, nsub_max, grid, num_cus, stream);
   return hipErrorInvalidValue;
 }
 
