@@ -55,6 +55,8 @@ def parse():
                     help="no GPU run: read two rocprofv3 --pmc result folders (FETCH_SIZE, "
                          "WRITE_SIZE) of this same command with --copy-calib-mib, and store "
                          "the dominant kernel's HBM bytes per call in profiles/traffic.json")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the secondary timing of the same steps replayed from a HIP graph")
     ap.add_argument("--first-call-check", action="store_true",
                     help="after the measurement, call the layer at never-seen token counts "
                          "(1..64, 100, 257, 4096, shuffled) and compare each first call with "
@@ -263,6 +265,35 @@ def oracle_and_parity(cfg, m, w, tk, budget):
     return cpu, parity
 
 
+def graph_replay(mods, x, lg, out, steps):
+    """Secondary timing: one call per weight copy captured into a HIP graph
+    (torch.cuda.CUDAGraph), the graphs replayed in turn for the same number of
+    steps; every replay's output is checked against the eager call's."""
+    import torch
+    torch.cuda.synchronize()
+    ref = [m(x, lg).clone() for m in mods]                 # eager results per copy
+    outs = [torch.empty_like(out) for _ in mods]
+    graphs = []
+    for m, o in zip(mods, outs):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            m(x, lg, out=o)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ok = True
+    for i, g in enumerate(graphs * 2):                      # replays with checks between
+        g.replay()
+        torch.cuda.synchronize()
+        j = i % len(graphs)
+        ok = ok and bool(torch.equal(outs[j], ref[j]))
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    return {"ms_per_step": round(ms, 4), "replays_match_eager": ok}
+
+
 def first_call_check(cfg, m, T_done, dev, stream):
     """First call at each never-seen token count against the p95 of the ten
     calls that follow it (same process, workspace sized beforehand so no call
@@ -401,6 +432,7 @@ def main():
     roof["algorithmic_bytes"] = work.stage_bytes[dom]
     roof["algorithmic_flops"] = work.stage_flops[dom]
 
+    graph = None if args.no_graph else graph_replay(mods, x, lg, out, args.steps)
     first_call = first_call_check(cfg, mods[0], T, dev, stream) if args.first_call_check else None
 
     cpu = parity = None
@@ -435,6 +467,7 @@ def main():
                   "step_us_with_all_stage_events_p95": round(float(np.percentile(step_us, 95)), 2)},
         "stages_us": stage_us,
         "parity": parity,
+        "graph": graph,
         "first_call": first_call,
         "source_digest": source_digest(),
     }

@@ -242,6 +242,39 @@ def test_fused_fp8_prefill_zipf_sampled():
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("over,T", [
+    (dict(H=2048, I=1040, E=16, K=4), 7),   # front launch (T <= 16)
+    (dict(H=2048, I=1040, E=16, K=4), 40),  # router, act quant and align launches
+    (dict(), 300),                          # tiled products
+])
+def test_fused_graph_replay_matches_eager(over, T, wdtype):
+    """The fused forward captured into a HIP graph: every replay, with eager
+    calls on other inputs in between, gives the eager call's bits (the library
+    records no memset and allocates nothing, so its launches replay as is)."""
+    cfg = replace(TINY, name="graph", **over)
+    w = _weights(cfg, wdtype, "cpu")
+    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"))
+    tk = workloads.make_tokens(cfg, T, seed=5)
+    x, lg = tk["x"].to(DEV), tk["logits"].to(DEV)
+    other = workloads.make_tokens(cfg, T, seed=6)
+    xo, lgo = other["x"].to(DEV), other["logits"].to(DEV)
+    say("graph replay", over, T, wdtype)
+    ref = m(x, lg).clone()
+    m.workspace(T, x.device)                 # sized before capture
+    out = torch.empty_like(ref)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m(x, lg, out=out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+        m(xo, lgo)                           # eager work on the same workspace
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 7),   # row tails in both products
     (dict(H=144, I=48, E=6, K=3), 40),
     (dict(), 300),
