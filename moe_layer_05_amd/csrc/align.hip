@@ -6,10 +6,9 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int P, int E, AlignOut small, AlignOut big, int thr,
-    int32_t* __restrict__ rank) {
+    const int32_t* __restrict__ ids, int P, int E, AlignOut out, int32_t* __restrict__ rank) {
   extern __shared__ int smem[];
-  align_block(ids, P, E, small, big, thr, rank, smem);
+  align_block(ids, P, E, out, rank, smem);
 }
 
 // ---- Multi-workgroup form, for many pairs.  (1) Each workgroup ranks the
@@ -161,10 +160,8 @@ size_t align_lds_bytes(int E) { return align_lds_words(E) * sizeof(int); }
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream) {
-  AlignOut small{sorted_ids, block_expert, num_post_pad, BM};
-  AlignOut big{nullptr, nullptr, nullptr, 256};
-  align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, small, big,
-                                                                 0x7FFFFFFF, rank);
+  AlignOut out{sorted_ids, block_expert, num_post_pad, BM};
+  align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, out, rank);
   return hipGetLastError();
 }
 

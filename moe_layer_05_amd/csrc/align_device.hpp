@@ -15,12 +15,8 @@
 // counts of earlier waves plus the in-wave rank.  Every step is a pure
 // function of the input order, so the layout is deterministic and stable.
 //
-// Split form: experts with at least `thr` pairs are laid out in a second,
-// separate layout padded to a larger block size, for the tiled products; the
-// others keep the small blocks.  With thr beyond the pair count every expert
-// is small and the result is the plain layout above.  (The fused forward
-// builds the split layouts for prefill with the multi-workgroup kernels of
-// align.hip, which give the same result.)
+// (At prefill sizes the fused forward lays out two layouts at once, split by
+// the experts' pair counts, with the multi-workgroup kernels of align.hip.)
 #pragma once
 
 #include "device_common.hpp"
@@ -70,14 +66,12 @@ __device__ __forceinline__ int2 block_exclusive_scan2(int v0, int v1, int* wsum,
 // The whole align step by one workgroup of kAlignThreads threads; `smem`
 // holds align_lds_words(E) ints.  `ids` may have been written earlier in the
 // same kernel by this workgroup (a workgroup barrier must separate them).
-__device__ __forceinline__ void align_block(const int32_t* ids, int P, int E, AlignOut small,
-                                            AlignOut big, int thr, int32_t* __restrict__ rank,
-                                            int* smem) {
+__device__ __forceinline__ void align_block(const int32_t* ids, int P, int E, AlignOut out,
+                                            int32_t* __restrict__ rank, int* smem) {
   int* cnt = smem;                                   // [E] running counts
-  int* seg = smem + E;                               // [E] segment starts (small)
-  int* segb = smem + 2 * E;                          // [E] segment starts (big)
-  int* wsum = smem + 3 * E;                          // [2][16] scan scratch
-  uint8_t* wc = reinterpret_cast<uint8_t*>(smem + 3 * E + 2 * kAlignWaves);  // [16][E]
+  int* seg = smem + E;                               // [E] segment starts
+  int* wsum = smem + 2 * E;                          // [2][16] scan scratch
+  uint8_t* wc = reinterpret_cast<uint8_t*>(smem + 2 * E + 2 * kAlignWaves);  // [16][E]
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -123,45 +117,30 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int P, int E, Al
     __syncthreads();
   }
 
-  // Exclusive scans of the padded counts over experts (E <= 1024: one each),
-  // one per layout.
+  // Exclusive scan of the padded counts over experts (E <= 1024: one each).
   const int c_e = (tid < E) ? cnt[tid] : 0;
-  const bool is_big = c_e >= thr;
-  const int pad_s = (!is_big) ? (c_e + small.BM - 1) / small.BM * small.BM : 0;
-  const int pad_b = is_big ? (c_e + big.BM - 1) / big.BM * big.BM : 0;
+  const int pad = (c_e + out.BM - 1) / out.BM * out.BM;
   int2 tot;
-  const int2 start = block_exclusive_scan2(pad_s, pad_b, wsum, &tot);
-  const int start_s = start.x, start_b = start.y, tot_s = tot.x, tot_b = tot.y;
-  if (tid < E) {
-    seg[tid] = start_s;
-    segb[tid] = start_b;
-  }
-  if (tid == 0) {
-    small.num_post_pad[0] = tot_s;
-    if (big.num_post_pad) big.num_post_pad[0] = tot_b;
-  }
-  if (tid < E && pad_s > 0) {
-    for (int b = 0; b < pad_s / small.BM; ++b) small.block_expert[start_s / small.BM + b] = tid;
-    for (int q = start_s + c_e; q < start_s + pad_s; ++q) small.sorted_ids[q] = P;
-  }
-  if (tid < E && pad_b > 0) {
-    for (int b = 0; b < pad_b / big.BM; ++b) big.block_expert[start_b / big.BM + b] = tid;
-    for (int q = start_b + c_e; q < start_b + pad_b; ++q) big.sorted_ids[q] = P;
+  const int start = block_exclusive_scan2(pad, 0, wsum, &tot).x;
+  if (tid < E) seg[tid] = start;
+  if (tid == 0) out.num_post_pad[0] = tot.x;
+  if (tid < E && pad > 0) {
+    for (int b = 0; b < pad / out.BM; ++b) out.block_expert[start / out.BM + b] = tid;
+    for (int q = start + c_e; q < start + pad; ++q) out.sorted_ids[q] = P;
   }
   __syncthreads();
 
   for (int i = tid; i < P; i += kAlignThreads) {
     const int e = i < kAlignThreads ? e0 : ids[i];
     const int r = i < kAlignThreads ? r0 : rank[i];
-    if (cnt[e] >= thr) big.sorted_ids[segb[e] + r] = i;
-    else small.sorted_ids[seg[e] + r] = i;
+    out.sorted_ids[seg[e] + r] = i;
   }
 }
 
-// LDS of align_block: counts, two segment starts, scan scratch (ints) and the
+// LDS of align_block: counts, segment starts, scan scratch (ints) and the
 // per-wave counts (bytes).
 constexpr size_t align_lds_words(int E) {
-  return (size_t)(3 * E + 2 * kAlignWaves) + ((size_t)kAlignWaves * E + 3) / 4;
+  return (size_t)(2 * E + 2 * kAlignWaves) + ((size_t)kAlignWaves * E + 3) / 4;
 }
 
 }  // namespace moe

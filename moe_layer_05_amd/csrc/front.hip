@@ -101,8 +101,7 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
                      a.ids + (int64_t)wave * a.K, a.wts + (int64_t)wave * a.K);
   __syncthreads();              // ids visible to the workgroup
 
-  AlignOut none{nullptr, nullptr, nullptr, 256};
-  align_block(a.ids, a.T * a.K, a.E, a.out, none, 0x7FFFFFFF, a.rank, smem);
+  align_block(a.ids, a.T * a.K, a.E, a.out, a.rank, smem);
 }
 
 template <bool FP8>
