@@ -165,6 +165,7 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t K,
   if (E > kMaxE || K > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
   return hip_status(
       launch_router(logits, T, E, K, renormalize, topk_ids, topk_weights, nullptr, 0, stream));
 }
@@ -190,6 +191,7 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t K, int32_t E, i
   if (T > 0 && (!topk_ids || !sorted_ids || !block_expert || !workspace)) return MOE_ERR_NULL;
   if (workspace_bytes < moe_align_workspace_bytes(T, K, E, block_m)) return MOE_ERR_WORKSPACE;
   if (T == 0) return MOE_OK;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_align(topk_ids, (int)(T * K), E, block_m, sorted_ids, block_expert,
                                  num_post_pad, static_cast<int32_t*>(workspace), stream));
 }
@@ -204,6 +206,7 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* sc
   if (n > 0 && (!x || !codes)) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
   if (workspace_bytes < moe_act_quant_workspace_bytes()) return MOE_ERR_WORKSPACE;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
   uint32_t* amax = static_cast<uint32_t*>(workspace);
   const int cus = num_cus();
   hipError_t e = launch_zero_amax(amax, 1, stream);

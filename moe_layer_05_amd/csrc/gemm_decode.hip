@@ -670,12 +670,13 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
   }
 }
 
+// Kernel preparation (dynamic LDS limits), run once per device by the entry
+// points before any launch (prepare_decode_kernels).
 template <int MODE, bool FP8, int NSUB, int RA, int D>
 hipError_t ready_one() {
-  static const hipError_t attr =
-      prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D>),
-                     D * (RA + NSUB) * kTileBytes);
-  return attr;
+  return prepare_kernel(
+      reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D>),
+      D * (RA + NSUB) * kTileBytes);
 }
 
 // LDS of the stream form: the ring and the id slots for cps chunks per unit.
@@ -685,17 +686,14 @@ constexpr int stream_lds(int d, int tiles, int cps) {
 
 template <int MODE, bool FP8, int NSUB, int RA, int D>
 hipError_t ready_stream() {                        // the limit for the most slots (cps = 1)
-  static const hipError_t attr =
-      prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
-                     stream_lds(D, RA + NSUB, 1));
-  return attr;
+  return prepare_kernel(
+      reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
+      stream_lds(D, RA + NSUB, 1));
 }
 
 template <int MODE, bool FP8, int NSUB, int RA, int D>
 hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
   const int lds = D * (RA + NSUB) * kTileBytes;
-  const hipError_t attr = ready_one<MODE, FP8, NSUB, RA, D>();
-  if (attr != hipSuccess) return attr;
   moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D><<<grid, dim3(64), lds, stream>>>(p);
   return hipGetLastError();
 }
@@ -714,8 +712,6 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
   const bool stream_ok = DS > 1 && nchunks % p.splits == 0 && cps >= 1 &&
                          grid.x >= 2 * resident && grid.x < 8 * resident;
   if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, DC>(p, grid, stream);
-  const hipError_t attr = ready_stream<MODE, FP8, NSUB, RA, DS>();
-  if (attr != hipSuccess) return attr;
   const unsigned g = (unsigned)std::min<int64_t>(grid.x, resident);
   moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, DS><<<dim3(g), dim3(64), lds, stream>>>(p);
   return hipGetLastError();

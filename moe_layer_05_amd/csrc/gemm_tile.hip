@@ -336,17 +336,15 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   }
 }
 
+// Run once per device by the entry points before any launch
+// (prepare_tile_kernels): the 128 KB LDS limit.
 template <int MODE, bool FP8>
 hipError_t ready_tile() {
-  static const hipError_t attr =
-      prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FP8>), kTileLds);
-  return attr;
+  return prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FP8>), kTileLds);
 }
 
 template <int MODE, bool FP8>
 hipError_t launch_tile(const GemmParams& p, dim3 grid, hipStream_t stream) {
-  const hipError_t attr = ready_tile<MODE, FP8>();
-  if (attr != hipSuccess) return attr;
   moe_gemm_tile_kernel<MODE, FP8><<<grid, dim3(64 * kWaves), kTileLds, stream>>>(p);
   return hipGetLastError();
 }

@@ -83,7 +83,9 @@ hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* 
 // Resolve a kernel in the runtime ahead of its first launch (with the dynamic
 // LDS limit it needs when lds > 0): the first launch of a kernel otherwise
 // pays the runtime's lookup, which a first call at a new token count would
-// show.  Each file prepares every kernel it may launch.
+// show.  Each file prepares every kernel it may launch; the entry points run
+// all of it once per device before their first launch there, which also sets
+// the LDS limits the GEMM launches rely on.
 inline hipError_t prepare_kernel(const void* fn, int lds) {
   if (lds > 0) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   hipFuncAttributes attr;
