@@ -94,11 +94,22 @@ def fp8_codes_per_expert(w):
     return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
 
 
-def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8):
+def fp8_codes_per_row(w):
+    """(uint8 codes, float32 scales [E, R]) of float32 weights [E, R, C]; one
+    scale per expert row (output channel), amax / 448, via torch's
+    float8_e4m3fn cast."""
+    amax = w.abs().amax(dim=2).to(torch.float32)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    q = (w / scale.unsqueeze(2)).clamp_(-FP8_MAX, FP8_MAX)
+    return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
+
+
+def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8, scales="tensor"):
     """Expert weights of ``cfg``.
 
     Returns a dict with w13 [E, 2I, H] and w2 [E, H, I] (float32, bfloat16 or
-    uint8 E4M3 codes) and, for E4M3, w13_scale and w2_scale [E] float32.
+    uint8 E4M3 codes) and, for E4M3, w13_scale and w2_scale: [E] float32, or
+    with ``scales="row"`` one per output row, [E, 2I] and [E, H].
     ``wdtype`` overrides the configuration's storage type (the tiny float32
     case is also run as bfloat16 and as E4M3).  Experts are drawn ``chunk`` at a
     time to bound the float32 staging memory; the stream order is w13 of the
@@ -112,15 +123,17 @@ def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8):
              "fp8": torch.uint8}[wdtype]
     w13 = torch.empty(E, 2 * I, H, dtype=store, device=device)
     w2 = torch.empty(E, H, I, dtype=store, device=device)
-    sc13 = torch.empty(E, dtype=torch.float32, device=device)
-    sc2 = torch.empty(E, dtype=torch.float32, device=device)
+    rows = scales == "row"
+    sc13 = torch.empty((E, 2 * I) if rows else (E,), dtype=torch.float32, device=device)
+    sc2 = torch.empty((E, H) if rows else (E,), dtype=torch.float32, device=device)
+    quant = fp8_codes_per_row if rows else fp8_codes_per_expert
     for e0 in range(0, E, chunk):
         e1 = min(E, e0 + chunk)
         a = torch.randn(e1 - e0, 2 * I, H, generator=g, device=device) * s13
         b = torch.randn(e1 - e0, H, I, generator=g, device=device) * s2
         if wdtype == "fp8":
-            w13[e0:e1], sc13[e0:e1] = fp8_codes_per_expert(a)
-            w2[e0:e1], sc2[e0:e1] = fp8_codes_per_expert(b)
+            w13[e0:e1], sc13[e0:e1] = quant(a)
+            w2[e0:e1], sc2[e0:e1] = quant(b)
         else:
             w13[e0:e1] = a.to(store)
             w2[e0:e1] = b.to(store)

@@ -1,4 +1,5 @@
-"""FP8 E4M3 codec, per-tensor quantiser and bfloat16 rounding (oracle).
+"""FP8 E4M3 codec, per-tensor and per-row quantisers and bfloat16 rounding
+(oracle).
 
 TEST INFRASTRUCTURE ONLY -- see ``oracle/__init__.py``.
 
@@ -99,6 +100,26 @@ def quantize(v, scale=None):
     s = per_tensor_scale(v32) if scale is None else np.float32(scale)
     q = (v32 / s).astype(np.float32)
     return encode(q), s
+
+
+def quantize_rows(v):
+    """(codes, scales) of the E4M3 quantisation of each row with its own scale.
+
+    The finer granularity the kongchang.com page motivates in "Triton Backend
+    Routing: A Practical Path to FP8 Quantization" (experts, and channels or
+    tokens within them, differ in their numerical distributions): row r gets
+    s_r = amax|v_r| / 448 (``per_tensor_scale`` of the row alone) and codes
+    encode(v_r / s_r).  ``v`` is [R, C]; returns codes [R, C] uint8 and scales
+    [R] float32.
+    """
+    v32 = np.asarray(v, dtype=np.float32)
+    if v32.ndim != 2:
+        raise ValueError("quantize_rows expects a 2-D array")
+    codes = np.empty(v32.shape, dtype=np.uint8)
+    scales = np.empty(v32.shape[0], dtype=np.float32)
+    for r in range(v32.shape[0]):
+        codes[r], scales[r] = quantize(v32[r])
+    return codes, scales
 
 
 def dequantize(codes, scale):

@@ -125,9 +125,23 @@ def align(ids, E, block_m):
 # a0: activation quantisation (FP8 mode)
 # --------------------------------------------------------------------------
 
-def act_quant(x):
-    """Per-tensor E4M3 quantisation of the activations: (codes uint8, scale)."""
-    return _fp8.quantize(np.asarray(x, dtype=np.float32))
+def act_quant(x, scales="tensor"):
+    """E4M3 quantisation of the activations: (codes uint8, scale).
+
+    scales == "tensor": one scale for the whole [T, H] tensor (float32).
+    scales == "row":    one scale per token row, [T] float32.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    if scales == "row":
+        return _fp8.quantize_rows(x32)
+    return _fp8.quantize(x32)
+
+
+def _dequant(codes, scale, scales):
+    """codes times the tensor scale, or times each row's scale."""
+    if scales == "row":
+        return _fp8.decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
+    return _fp8.decode(codes) * np.float64(scale)
 
 
 # --------------------------------------------------------------------------
@@ -140,10 +154,16 @@ def silu(z):
 
 
 def _weight(wt, e, scale, fp8_mode, dtype):
-    """Expert weight matrix in ``dtype``: code * scale (FP8) or the value."""
+    """Expert weight matrix in ``dtype``: code * scale (FP8) or the value.
+
+    ``scale[e]`` is the expert tensor's scale, or an array with one scale per
+    output row (per-channel scales: [2I] for w13, [H] for w2)."""
     m = np.asarray(wt[e])
     if fp8_mode:
-        return (_fp8.decode(m) * np.float64(scale[e])).astype(dtype)
+        se = np.asarray(scale[e], dtype=np.float64)
+        if se.ndim == 1:
+            return (_fp8.decode(m) * se[:, None]).astype(dtype)
+        return (_fp8.decode(m) * np.float64(se)).astype(dtype)
     return m.astype(dtype)
 
 
@@ -156,7 +176,7 @@ def _gate_up(xh, W13, I):
 
 def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
                 w2_scale=None, renormalize=True, dtype=np.float64,
-                tokens=None, return_parts=False, workers=1):
+                tokens=None, return_parts=False, workers=1, act_scales="tensor"):
     """The layer output for the tokens in ``tokens`` (all by default).
 
     x       [T, H] float values (the bfloat16 activations as float32).
@@ -164,7 +184,11 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     w13     indexable by expert -> [2I, H]; float values, or uint8 E4M3 codes
             when wdtype == "fp8".
     w2      indexable by expert -> [H, I]; same convention.
-    w13_scale, w2_scale  [E] float32 per-expert-tensor scales (FP8 only).
+    w13_scale, w2_scale  [E] float32 per-expert-tensor scales (FP8 only), or
+            per-channel scales [E, 2I] / [E, H] (one per output row).
+    act_scales  "tensor": one scale for x and one for the intermediate a over
+            all routed pairs; "row": one per token row of x and one per pair
+            row of a (FP8 only).
     dtype   arithmetic precision of the products (float64 by default).
     workers experts evaluated concurrently (same arithmetic, less wall time).
 
@@ -185,13 +209,15 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     parts = {"ids": ids, "weights": wts}
 
     if fp8_mode:
-        qx, s_x = act_quant(x32)
-        xh = (_fp8.decode(qx) * np.float64(s_x)).astype(dtype)
+        qx, s_x = act_quant(x32, act_scales)
+        xh = _dequant(qx, s_x, act_scales).astype(dtype)
         parts["s_x"] = s_x
     else:
         xh = x32.astype(dtype)
 
-    need_all = fp8_mode
+    # a per-tensor intermediate scale needs every routed pair; per-pair
+    # scales do not
+    need_all = fp8_mode and act_scales == "tensor"
     want = np.zeros(T, dtype=bool)
     want[tokens] = True
 
@@ -216,8 +242,8 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     if fp8_mode and a:
         keys = sorted(a)
         amat = np.stack([a[kk] for kk in keys]).astype(np.float32)
-        qa, s_a = _fp8.quantize(amat)
-        ah = _fp8.decode(qa) * np.float64(s_a)
+        qa, s_a = act_quant(amat, act_scales)
+        ah = _dequant(qa, s_a, act_scales)
         for r, kk in enumerate(keys):
             a[kk] = ah[r].astype(dtype)
         parts["s_a"] = s_a
@@ -246,7 +272,7 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
 
 
 def moe_dense(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
-              w2_scale=None, renormalize=True, dtype=np.float64):
+              w2_scale=None, renormalize=True, dtype=np.float64, act_scales="tensor"):
     """The same layer written as "run every expert on every token, mask".
 
     y_t = sum_e M[t, e] * expert_e(x_t), with M[t, e] the routing weight of e
@@ -266,8 +292,8 @@ def moe_dense(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
             M[t, ids[t, k]] = wts[t, k]
             routed[t, ids[t, k]] = True
     if fp8_mode:
-        qx, s_x = act_quant(x32)
-        xh = (_fp8.decode(qx) * np.float64(s_x)).astype(dtype)
+        qx, s_x = act_quant(x32, act_scales)
+        xh = _dequant(qx, s_x, act_scales).astype(dtype)
     else:
         xh = x32.astype(dtype)
     A = []
@@ -276,7 +302,12 @@ def moe_dense(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
         I = W13.shape[0] // 2
         A.append(_gate_up(xh, W13, I))       # [T, I] for every token
     A = np.stack(A, axis=1)                  # [T, E, I]
-    if fp8_mode:
+    if fp8_mode and act_scales == "row":
+        # every (token, expert) row on its own scale; unrouted rows are masked
+        flat = A.reshape(T * E, -1).astype(np.float32)
+        q, s_rows = _fp8.quantize_rows(flat)
+        A = (_fp8.decode(q) * s_rows.astype(np.float64)[:, None]).reshape(A.shape)
+    elif fp8_mode:
         amax_src = A[routed].astype(np.float32)
         s_a = _fp8.per_tensor_scale(amax_src)
         q, _ = _fp8.quantize(A.astype(np.float32), scale=s_a)

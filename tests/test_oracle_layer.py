@@ -17,6 +17,7 @@ import torch
 import torch.nn.functional as F
 from scipy.special import softmax
 
+from moe_layer_05_amd import workloads
 from oracle import fp8, moe
 from tests.helpers import np_f32, np_u8, oracle_inputs, tiny_case
 
@@ -245,3 +246,71 @@ def test_fp8_scale_is_per_call():
     _, alone = moe.moe_forward(K=cfg.K, return_parts=True, **one)
     assert not np.allclose(both["y"][1], alone["y"][0], rtol=1e-3)
     assert both["s_x"] > alone["s_x"]
+
+
+# ------------------------------------------------------------------ per-row scales
+# Finer FP8 granularity: one scale per weight output row (channel) and one per
+# activation row (token of x, pair of the intermediate).
+
+def _row_case(T=5, **over):
+    cfg, _, tk = tiny_case("fp8", T=T, **over)
+    w = workloads.make_weights(cfg, seed=0, device="cpu", wdtype="fp8", scales="row")
+    return cfg, w, tk
+
+
+def test_fp8_row_scales_reduce_to_tensor_scales():
+    """One token, one expert per token, every row scale equal to the tensor
+    scale: the per-row layer is the per-tensor layer, bit for bit."""
+    cfg, w, tk = tiny_case("fp8", T=1, K=1)
+    kw = oracle_inputs(w, tk)
+    ref = moe.moe_forward(K=1, **kw)
+    I, H = cfg.I, cfg.H
+    kw["w13_scale"] = np.repeat(kw["w13_scale"][:, None], 2 * I, axis=1)
+    kw["w2_scale"] = np.repeat(kw["w2_scale"][:, None], H, axis=1)
+    got = moe.moe_forward(K=1, act_scales="row", **kw)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_fp8_row_mode_sparse_equals_dense():
+    cfg, w, tk = _row_case(T=6)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, act_scales="row", **kw)
+    yd = moe.moe_dense(K=cfg.K, act_scales="row", **kw)
+    assert np.allclose(p["y"], yd, rtol=1e-12, atol=1e-14)
+
+
+def test_fp8_row_mode_tokens_are_independent():
+    """With per-token and per-pair scales no scale couples the tokens: each
+    token run alone gives exactly its row of the batched run."""
+    cfg, w, tk = _row_case(T=5)
+    kw = oracle_inputs(w, tk)
+    full = moe.moe_forward(K=cfg.K, act_scales="row", **kw)
+    for t in range(5):
+        one = dict(kw, x=kw["x"][t:t + 1], logits=kw["logits"][t:t + 1])
+        row = moe.moe_forward(K=cfg.K, act_scales="row", **one)
+        assert np.array_equal(row[0].view(np.uint32), full[t].view(np.uint32))
+
+
+def test_fp8_row_scales_of_x_and_a():
+    cfg, w, tk = _row_case(T=4)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, act_scales="row", **kw)
+    amax = np.abs(kw["x"]).max(axis=1).astype(np.float32)
+    assert np.array_equal(p["s_x"], (amax / np.float32(448.0)).astype(np.float32))
+    assert p["s_a"].shape == (4 * cfg.K,)
+
+
+def test_fp8_row_weight_scale_scales_its_output_column():
+    """Doubling the scale of w2 row h doubles output column h exactly (before
+    the bfloat16 rounding) and leaves the other columns unchanged."""
+    cfg, w, tk = _row_case(T=3)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, act_scales="row", **kw)
+    h = 5
+    s2 = kw["w2_scale"].copy()
+    s2[:, h] *= 2
+    _, q = moe.moe_forward(K=cfg.K, return_parts=True, act_scales="row",
+                           **dict(kw, w2_scale=s2))
+    assert np.array_equal(q["y"][:, h], 2 * p["y"][:, h])
+    others = np.arange(cfg.H) != h
+    assert np.array_equal(q["y"][:, others], p["y"][:, others])
