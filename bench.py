@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--T", type=int, default=None,
                     help="tokens per batch (default: the largest decode batch, "
                          "or 4096 for the prefill workload)")
+    ap.add_argument("--scales", choices=("tensor", "row"), default="tensor",
+                    help="FP8 workloads: one scale per expert tensor (and per activation "
+                         "tensor), or one per weight row and per activation row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work the cpu_baseline sample aims at")
@@ -80,7 +83,11 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload, T, kernel):
+def traffic_key(workload, T, scales):
+    return f"{workload}/T{T}" + ("/row_scales" if scales == "row" else "")
+
+
+def load_traffic(workload, T, kernel, scales="tensor"):
     """HBM bytes per launch of ``kernel`` from the committed counter runs, or
     None when there are none for this workload or the kernels have changed."""
     try:
@@ -88,7 +95,7 @@ def load_traffic(workload, T, kernel):
             db = json.load(fh)
     except (OSError, ValueError):
         return None
-    rec = db.get(f"{workload}/T{T}")
+    rec = db.get(traffic_key(workload, T, scales))
     if not rec or rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
         return None
     return rec.get("bytes_per_launch")
@@ -146,35 +153,42 @@ def record_traffic(args):
             db = json.load(fh)
     except (OSError, ValueError):
         db = {}
-    db[f"{cfg.name}/T{T}"] = rec
+    key = traffic_key(cfg.name, T, args.scales)
+    db[key] = rec
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(db, fh, indent=1, sort_keys=True)
         fh.write("\n")
-    print(json.dumps({f"{cfg.name}/T{T}": rec}))
+    print(json.dumps({key: rec}))
 
 
 class Work:
     """Sizes and algorithmic work of one call, from the actual routing."""
 
-    def __init__(self, cfg, T, ids):
+    def __init__(self, cfg, T, ids, rows=False):
         import numpy as np
         self.cfg, self.T = cfg, T
         fp8 = cfg.wdtype == "fp8"
+        rows = rows and fp8
         bw = 1 if fp8 else 2
         H, I, E, K = cfg.H, cfg.I, cfg.E, cfg.K
         P = T * K
         self.active = int(np.unique(ids).size)
         w13_e, w2_e = 2 * I * H * bw, H * I * bw
-        sc = 8 if fp8 else 0
+        # weight scales per expert: one per tensor, or one per row (float32)
+        sc13, sc2 = ((2 * I * 4, H * 4) if rows else (4, 4)) if fp8 else (0, 0)
+        # activation scales read by each product: per token row of x, per pair row of a
+        sx, sa = (T * 4, P * 4) if rows else (0, 0)
         # whole layer: active experts' weights (+ scales), x, logits, out
-        self.layer_bytes = self.active * (w13_e + w2_e + sc) + T * H * 2 + T * E * 4 + T * H * 2
+        self.layer_bytes = (self.active * (w13_e + w2_e + sc13 + sc2) + T * H * 2 + T * E * 4
+                            + T * H * 2)
         self.layer_flops = 6.0 * H * I * P
         # gate/up kernel: its experts' w13, the x rows (E4M3 codes or bf16)
         # and the intermediate it writes (float32 for the FP8 path, bf16 else)
         self.stage_bytes = {
-            "gate_up": self.active * (w13_e + sc // 2) + T * H * (1 if fp8 else 2)
+            "gate_up": self.active * (w13_e + sc13) + T * H * (1 if fp8 else 2) + sx
                        + P * I * (4 if fp8 else 2),
-            "down": self.active * (w2_e + sc // 2) + P * I * (1 if fp8 else 2) + P * H * 4 + P * 4,
+            "down": self.active * (w2_e + sc2) + P * I * (1 if fp8 else 2) + sa + P * H * 4
+                    + P * 4,
         }
         self.stage_flops = {"gate_up": 4.0 * H * I * P, "down": 2.0 * H * I * P}
         self.kind = "fp8" if fp8 else "bf16"
@@ -221,7 +235,7 @@ def host_weights(w):
     return Experts(w)
 
 
-def oracle_and_parity(cfg, m, w, tk, budget):
+def oracle_and_parity(cfg, m, w, tk, budget, scales="tensor"):
     """Time the CPU oracle on sub-batches of the first n tokens (n doubling
     while the last run stays well inside ``budget`` seconds), and compare the
     library on the same sub-batch.  Returns (cpu_baseline, parity)."""
@@ -243,7 +257,8 @@ def oracle_and_parity(cfg, m, w, tk, budget):
         xh = x.float().cpu().numpy()
         lh = lg.cpu().numpy()
         t0 = time.perf_counter()
-        ref, parts = omoe.moe_forward(xh, lh, K=cfg.K, return_parts=True, **kw)
+        ref, parts = omoe.moe_forward(xh, lh, K=cfg.K, return_parts=True,
+                                      act_scales=scales if fp8 else "tensor", **kw)
         dt = time.perf_counter() - t0
         last = (n, dt, ref, parts, x, lg)
         log(f"oracle sub-batch of {n} tokens: {dt:.2f} s")
@@ -363,7 +378,9 @@ def main():
         log(f"copy calibration: {args.copy_calib_mib} MiB read + written once")
 
     wdtype = "bf16" if cfg.wdtype == "float32" else cfg.wdtype
-    w = workloads.make_weights(cfg, seed=0, device=dev, wdtype=wdtype)
+    rows = args.scales == "row" and wdtype == "fp8"
+    w = workloads.make_weights(cfg, seed=0, device=dev, wdtype=wdtype,
+                               scales="row" if rows else "tensor")
     tk = workloads.make_tokens(cfg, T, seed=0, device=dev)
     wbytes = w["w13"].numel() * w["w13"].element_size() + w["w2"].numel() * w["w2"].element_size()
     # Rotate weight copies when one set could stay in the 256 MB last-level
@@ -377,7 +394,7 @@ def main():
     out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device=dev)
     _, ids, _ = mods[0](x, lg, out=out, return_topk=True)
     torch.cuda.synchronize()
-    work = Work(cfg, T, ids.cpu().numpy())
+    work = Work(cfg, T, ids.cpu().numpy(), rows)
 
     nst = len(binding.STAGES)
     stream = torch.cuda.current_stream()
@@ -442,7 +459,7 @@ def main():
     roof["kernel_us"] = round(dom_us, 2)
     roof["kernel_us_events_raw"] = round(dom_raw_us, 2)
     roof["event_pair_floor_us"] = round(event_floor_us, 2)
-    roof["traffic"] = load_traffic(cfg.name, T, dom)
+    roof["traffic"] = load_traffic(cfg.name, T, dom, "row" if rows else "tensor")
     roof["algorithmic_bytes"] = work.stage_bytes[dom]
     roof["algorithmic_flops"] = work.stage_flops[dom]
 
@@ -451,7 +468,8 @@ def main():
 
     cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu, parity = oracle_and_parity(cfg, mods[0], w, tk, args.cpu_budget)
+        cpu, parity = oracle_and_parity(cfg, mods[0], w, tk, args.cpu_budget,
+                                        "row" if rows else "tensor")
 
     gbps = work.layer_bytes / (ms * 1e-3) / 1e9
     line = {
@@ -469,6 +487,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "K": cfg.K, "weights": wdtype, "routing": cfg.routing,
+                   "fp8_scales": ("row" if rows else "tensor") if wdtype == "fp8" else None,
                    "active_experts": work.active, "weight_copies": copies},
         "roofline": roof,
         "cpu_baseline": cpu,

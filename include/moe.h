@@ -55,6 +55,14 @@ typedef enum {
   MOE_FP8_E4M3 = 1          /* expert weights are OCP E4M3 codes + scales   */
 } moe_wdtype;
 
+typedef enum {
+  MOE_SCALES_TENSOR = 0,    /* FP8: one scale per expert weight tensor, one for
+                               x and one for the intermediate               */
+  MOE_SCALES_ROW = 1        /* FP8: one scale per weight output row
+                               (channel), per token row of x and per pair
+                               row of the intermediate                      */
+} moe_fp8_scales;
+
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status s);
 
@@ -121,6 +129,24 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes,
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Activation quantisation with one scale per row (a0 under MOE_SCALES_ROW).
+ * Each row r of cols values is quantised on its own: scales[r] = amax|x_r| /
+ * 448 (1 when the row is all zero) and codes as in moe_act_quant_fp8 with
+ * that scale.  Finer granularity than one scale per tensor, read from the
+ * kongchang.com page, "Triton Backend Routing: A Practical Path to FP8
+ * Quantization" (numerical distributions differ, so a uniform scale loses
+ * precision), taken down to rows.
+ *
+ *   x       [rows, cols] bfloat16 (raw 16-bit patterns), 16-byte aligned
+ *   codes   [rows, cols] uint8 (out), 16-byte aligned
+ *   scales  [rows] float32 (out)
+ * Supported: cols % 8 == 0.  No workspace.
+ */
+moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols,
+                                  uint8_t* codes, float* scales,
+                                  hipStream_t stream);
+
+/*
  * Fused layer forward (a0..a6).  out[t] = bfloat16_rne( sum_k w[t,k] *
  *   W2_e (silu(W1_e x^_t) * (W3_e x^_t)) ),  e = topk_ids[t,k],
  * with W1_e = w13[e, 0:I, :] (gate) and W3_e = w13[e, I:2I, :] (up).
@@ -134,17 +160,26 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes,
  * kongchang.com page, "Swap-AB"; aib.vote page, second paragraph).
  *
  * MOE_BF16:     x^ = x; weights bfloat16.
- * MOE_FP8_E4M3: x^ = dequantised per-tensor E4M3 of x (as moe_act_quant_fp8);
+ * MOE_FP8_E4M3, fp8_scales == MOE_SCALES_TENSOR:
+ *               x^ = dequantised per-tensor E4M3 of x (as moe_act_quant_fp8);
  *               W = code * w13_scale[e] (or w2_scale[e]); the intermediate
  *               a = silu(g) * u is quantised per tensor over all pairs, from
  *               its float32 value, before the down projection.
+ * MOE_FP8_E4M3, fp8_scales == MOE_SCALES_ROW:
+ *               x^ = per-token-row E4M3 of x (as moe_act_quant_fp8_rows);
+ *               W[r, :] = code[r, :] * w13_scale[e, r] (w2_scale[e, r]); the
+ *               intermediate is quantised per pair row.  No scale couples two
+ *               tokens, so a token's output does not depend on the batch.
  *
  * Fields:
  *   x               [T, H] bfloat16
  *   router_logits   [T, E] float32
  *   w13             [E, 2I, H] bfloat16 or uint8 E4M3 codes
  *   w2              [E, H, I]  bfloat16 or uint8 E4M3 codes
- *   w13_scale, w2_scale  [E] float32, FP8 only (ignored for bf16, may be NULL)
+ *   fp8_scales      moe_fp8_scales, FP8 only (ignored for bf16)
+ *   w13_scale, w2_scale  FP8 only (ignored for bf16, may be NULL):
+ *                   [E] float32 with MOE_SCALES_TENSOR; [E, 2I] and [E, H]
+ *                   float32, 16-byte aligned, with MOE_SCALES_ROW
  *   out             [T, H] bfloat16 (out)
  *   topk_ids_out    [T, K] int32 (out, optional: NULL to skip)
  *   topk_weights_out[T, K] float32 (out, optional: NULL to skip)
@@ -155,6 +190,7 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes,
  */
 typedef struct {
   moe_wdtype wdtype;
+  moe_fp8_scales fp8_scales;
   int64_t T;
   int32_t H, I, E, K;
   int32_t renormalize;

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     FusedMoE,
     MoEError,
     act_quant_fp8,
+    act_quant_fp8_rows,
     align,
     align_capacity,
     fused_block_m,

@@ -16,6 +16,9 @@ LIB_PATH = os.path.join(HERE, "libmoemi.so")
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
 
+MOE_SCALES_TENSOR = 0
+MOE_SCALES_ROW = 1
+
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
           4: "MOE_ERR_WORKSPACE", 5: "MOE_ERR_HIP"}
 
@@ -29,6 +32,7 @@ class MoEError(RuntimeError):
 class FusedArgs(ctypes.Structure):
     _fields_ = [
         ("wdtype", ctypes.c_int),
+        ("fp8_scales", ctypes.c_int),
         ("T", ctypes.c_int64),
         ("H", ctypes.c_int32),
         ("I", ctypes.c_int32),
@@ -68,6 +72,9 @@ _SIGS = {
     "moe_act_quant_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]),
+    "moe_act_quant_fp8_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
     "moe_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FusedArgs)]),
     "moe_fused_block_m": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int]),
@@ -177,6 +184,19 @@ def act_quant_fp8(x, stream=None):
     return codes, scale
 
 
+def act_quant_fp8_rows(x, stream=None):
+    """(codes uint8 [R, C], scales [R] float32) of bfloat16 x [R, C], one
+    scale per row."""
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    xp = _dev(x, torch.bfloat16, "x")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+    _check(lib().moe_act_quant_fp8_rows(xp, x.shape[0], x.shape[1], _ptr(codes), _ptr(scales),
+                                        _stream(stream)), "moe_act_quant_fp8_rows")
+    return codes, scales
+
+
 # ------------------------------------------------------------------ a0..a6
 
 def fused_block_m(T, H, I, E, K, fp8):
@@ -187,8 +207,10 @@ class FusedMoE:
     """The fused layer forward bound to fixed weights.
 
     w13 [E, 2I, H] and w2 [E, H, I] are bfloat16, or uint8 E4M3 codes with
-    w13_scale / w2_scale [E] float32.  The workspace is a torch buffer grown
-    on demand and reused across calls (the library allocates nothing)."""
+    w13_scale / w2_scale float32: [E] (one scale per expert tensor, and per
+    tensor activation scales) or [E, 2I] / [E, H] (one per weight row, and
+    per row activation scales).  The workspace is a torch buffer grown on
+    demand and reused across calls (the library allocates nothing)."""
 
     def __init__(self, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True):
         self.fp8 = w13.dtype == torch.uint8
@@ -203,9 +225,15 @@ class FusedMoE:
         _dev(w2, want, "w2")
         if tuple(w2.shape) != (self.E, self.H, self.I):
             raise ValueError("w2 must be [E, H, I]")
+        self.rows = False
         if self.fp8:
             _dev(w13_scale, torch.float32, "w13_scale")
             _dev(w2_scale, torch.float32, "w2_scale")
+            self.rows = w13_scale.dim() == 2
+            want13 = (self.E, 2 * self.I) if self.rows else (self.E,)
+            want2 = (self.E, self.H) if self.rows else (self.E,)
+            if tuple(w13_scale.shape) != want13 or tuple(w2_scale.shape) != want2:
+                raise ValueError(f"scales must be {want13} and {want2}")
         self.w13_scale = w13_scale
         self.w2_scale = w2_scale
         self._ws = None
@@ -213,6 +241,7 @@ class FusedMoE:
     def args(self, x, logits, out, ids=None, wts=None):
         a = FusedArgs()
         a.wdtype = MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+        a.fp8_scales = MOE_SCALES_ROW if self.rows else MOE_SCALES_TENSOR
         a.T = x.shape[0]
         a.H, a.I, a.E, a.K = self.H, self.I, self.E, self.K
         a.renormalize = int(bool(self.renormalize))
@@ -230,6 +259,7 @@ class FusedMoE:
     def workspace_bytes(self, T):
         a = FusedArgs()
         a.wdtype = MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+        a.fp8_scales = MOE_SCALES_ROW if self.rows else MOE_SCALES_TENSOR
         a.T, a.H, a.I, a.E, a.K = T, self.H, self.I, self.E, self.K
         return int(lib().moe_fused_workspace_bytes(ctypes.byref(a)))
 

@@ -75,7 +75,7 @@ int64_t max_blocks(int64_t P, int E, int bm) {
 constexpr int kTileThreshold = 16;
 
 struct FusedLayout {
-  size_t ids, wts, sorted, bexp, npp, rank, scal, qx, a, qa, dw, ascr, total;
+  size_t ids, wts, sorted, bexp, npp, rank, scal, srow, qx, a, qa, dw, ascr, total;
   size_t sorted_t, bexp_t, npp_t;     // tiled layout (prefill)
   int bm;
   int64_t cap, nblk;
@@ -84,14 +84,19 @@ struct FusedLayout {
   DecodeShape gu, dn;
 };
 
+bool rows_mode(const moe_fused_args* a) {
+  return a->wdtype == MOE_FP8_E4M3 && a->fp8_scales == MOE_SCALES_ROW;
+}
+
 bool use_tiles(int64_t T, int E, int K) {
   return T >= 256 && T * (int64_t)K >= 32LL * E;
 }
 
-FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
+FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, bool rows) {
   FusedLayout L{};
   const int64_t P = T * K;
   const bool fp8 = wd == MOE_FP8_E4M3;
+  rows = rows && fp8;
   const int welem = fp8 ? 1 : 2;
   L.tiled = use_tiles(T, E, K);
   L.bm = L.tiled ? kTileThreshold : moe_fused_block_m(T, H, I, E, K, wd);
@@ -121,6 +126,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd) {
   L.rank = take(P * 4);
   L.ascr = take(L.tiled ? align_multi_workspace_bytes((int)P, E) : 0);
   L.scal = take(2 * kAmaxWords * 4);     // amax blocks of x and of a
+  L.srow = take(rows ? (size_t)(T + P) * 4 : 0);   // per-row scales of x and of a
   L.qx = take(fp8 ? (size_t)T * H : 0);
   L.a = take((size_t)P * I * (fp8 ? 4 : 2));
   L.qa = take(fp8 ? (size_t)P * I : 0);
@@ -215,6 +221,17 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* sc
   return hip_status(e);
 }
 
+moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols, uint8_t* codes,
+                                  float* scales, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return MOE_ERR_SHAPE;
+  if (cols % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_quant_rows(x, true, rows, cols, codes, scales, num_cus(), stream));
+}
+
 int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
                           moe_wdtype wdtype) {
   (void)H; (void)I; (void)wdtype;
@@ -233,7 +250,10 @@ size_t moe_fused_workspace_bytes(const moe_fused_args* a) {
   if (!a) return 0;
   if (check_shape(a->T, a->H, a->I, a->E, a->K) != MOE_OK) return 0;
   if (a->wdtype != MOE_BF16 && a->wdtype != MOE_FP8_E4M3) return 0;
-  return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype).total;
+  if (a->wdtype == MOE_FP8_E4M3 && a->fp8_scales != MOE_SCALES_TENSOR &&
+      a->fp8_scales != MOE_SCALES_ROW)
+    return 0;
+  return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype, rows_mode(a)).total;
 }
 
 }  // extern "C"
@@ -250,17 +270,21 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   moe_status st = check_shape(a->T, a->H, a->I, a->E, a->K);
   if (st != MOE_OK) return st;
   if (a->wdtype != MOE_BF16 && a->wdtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
-  if (a->T == 0) return MOE_OK;
   const bool fp8 = a->wdtype == MOE_FP8_E4M3;
+  if (fp8 && a->fp8_scales != MOE_SCALES_TENSOR && a->fp8_scales != MOE_SCALES_ROW)
+    return MOE_ERR_UNSUPPORTED;
+  if (a->T == 0) return MOE_OK;
+  const bool rows = rows_mode(a);
   if (!a->x || !a->router_logits || !a->w13 || !a->w2 || !a->out || !a->workspace)
     return MOE_ERR_NULL;
   if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_NULL;
+  if (rows && (!aligned16(a->w13_scale) || !aligned16(a->w2_scale))) return MOE_ERR_UNSUPPORTED;
   if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->out) ||
       !aligned16(a->workspace))
     return MOE_ERR_UNSUPPORTED;
   const int64_t T = a->T;
   const int H = a->H, I = a->I, E = a->E, K = a->K;
-  const FusedLayout L = fused_layout(T, H, I, E, K, a->wdtype);
+  const FusedLayout L = fused_layout(T, H, I, E, K, a->wdtype, rows);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
 
@@ -273,6 +297,8 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   int32_t* rank = reinterpret_cast<int32_t*>(ws + L.rank);
   uint32_t* amax_x = reinterpret_cast<uint32_t*>(ws + L.scal);   // amax blocks
   uint32_t* amax_a = amax_x + kAmaxWords;
+  float* sx = reinterpret_cast<float*>(ws + L.srow);             // [T] (per-row scales)
+  float* sa = sx + T;                                             // [P]
   uint8_t* qx = ws + L.qx;
   void* abuf = ws + L.a;
   uint8_t* qa = ws + L.qa;
@@ -289,19 +315,22 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     // a1 + a0 + a2 in one launch; the act-quant and align stages are empty
     if (e == hipSuccess)
       e = launch_front(a->router_logits, T, E, K, a->renormalize, ids, wts, fp8, a->x, H, amax_x,
-                       amax_a, qx, L.bm, sorted, bexp, npp, rank, stream);
+                       amax_a, qx, rows ? sx : nullptr, L.bm, sorted, bexp, npp, rank, stream);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
   } else {
     // a1 (also clears the amax slots of x and a for this call)
     if (e == hipSuccess)
       e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x,
-                        fp8 ? 2 : 0, stream);
+                        fp8 && !rows ? 2 : 0, stream);
     // a0
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
-    if (e == hipSuccess && fp8) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
-    if (e == hipSuccess && fp8)
-      e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
+    if (e == hipSuccess && rows) {
+      e = launch_quant_rows(a->x, true, T, H, qx, sx, cus, stream);
+    } else if (fp8) {
+      if (e == hipSuccess) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
+      if (e == hipSuccess) e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
+    }
     // a2
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
     if (e == hipSuccess) {
@@ -331,9 +360,11 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.groups = L.gu.groups;
     g.splits = L.gu.splits;
     g.w_scale = fp8 ? a->w13_scale : nullptr;
-    g.act_amax = fp8 ? amax_x + kAmaxFinal : nullptr;
+    g.row_scales = rows ? 1 : 0;
+    g.act_amax = fp8 && !rows ? amax_x + kAmaxFinal : nullptr;
+    g.act_scale = rows ? sx : nullptr;
     g.a_out = abuf;
-    g.a_amax = fp8 ? amax_a : nullptr;
+    g.a_amax = fp8 && !rows ? amax_a : nullptr;
     e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, cus, stream);
     if (e == hipSuccess && L.tiled) {
       GemmParams t = g;
@@ -348,7 +379,9 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   }
   // intermediate quantisation (FP8)
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_INTER_QUANT, stream);
-  if (e == hipSuccess && fp8)
+  if (e == hipSuccess && rows)
+    e = launch_quant_rows(abuf, false, P, I, qa, sa, cus, stream);
+  else if (e == hipSuccess && fp8)
     e = launch_quant_f32(static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus, stream);
   // a5
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);
@@ -361,7 +394,8 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.groups = L.dn.groups;
     g.splits = L.dn.splits;
     g.w_scale = fp8 ? a->w2_scale : nullptr;
-    g.act_amax = fp8 ? amax_a + kAmaxFinal : nullptr;
+    g.act_amax = fp8 && !rows ? amax_a + kAmaxFinal : nullptr;
+    g.act_scale = rows ? sa : nullptr;
     g.dw = dw;
     g.dw_split_stride = (int64_t)P * H;
     g.dw_bf16 = L.tiled ? 1 : 0;

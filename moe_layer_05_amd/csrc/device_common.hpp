@@ -39,6 +39,22 @@ __device__ __forceinline__ void store_part4(void* buf, bool bf16, int64_t idx, f
   }
 }
 
+// Per-row dequantisation scales of four consecutive weight rows r..r+3 (r a
+// multiple of 4, so one 16-byte load), each times the activation row's scale.
+__device__ __forceinline__ void row_scales4(const float* ws, int r, float sa, float (&out)[4]) {
+  const float4 w = *reinterpret_cast<const float4*>(ws + r);
+  out[0] = w.x * sa;
+  out[1] = w.y * sa;
+  out[2] = w.z * sa;
+  out[3] = w.w * sa;
+}
+// The same for a gate row group and its up row group.
+__device__ __forceinline__ void row_scales4(const float* ws, int rg, int ru, float sa,
+                                            float (&g)[4], float (&u)[4]) {
+  row_scales4(ws, rg, sa, g);
+  row_scales4(ws, ru, sa, u);
+}
+
 // ---------------------------------------------------------------- E4M3
 
 // float32 -> OCP E4M3 code: nearest, ties to the even mantissa, saturating to

@@ -13,7 +13,8 @@
 //    codes E4M3(x / s), s = amax / 448, of its own slice (the same arithmetic
 //    as the two-kernel path, so the codes are identical); workgroup 1 stores
 //    the final amax word for the GEMM epilogue and clears the slots of the
-//    intermediate's amax.
+//    intermediate's amax.  With per-row scales workgroup 1 + t quantises
+//    token row t on that row's own amax and stores its scale.
 #include "align_device.hpp"
 #include "internal.hpp"
 #include "route_device.hpp"
@@ -37,6 +38,7 @@ struct FrontArgs {
   uint32_t* amax_x;          // amax block of x (final word written here)
   uint32_t* amax_a;          // amax block of a (slots cleared here)
   uint2* qx;                 // codes of x, 8 per uint2
+  float* sx_rows;            // per-row scales of x [T], or nullptr for one scale
   // align
   AlignOut out;
   int32_t* rank;
@@ -54,6 +56,34 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
   const int lane = tid & (kWave - 1);
 
   if constexpr (FP8) {
+    if (blockIdx.x > 0 && a.sx_rows) {
+      // per-row scales: workgroup b quantises token row b - 1 on its own amax
+      const int64_t h8 = a.n8 / a.T;
+      const int64_t base = (int64_t)(blockIdx.x - 1) * h8;
+      float m = 0.0f;
+      for (int64_t j = tid; j < h8; j += kAlignThreads) {
+        const uint4 q = a.x[base + j];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(q.x)), fabsf(bf16_hi(q.x))),
+                           fmaxf(fabsf(bf16_lo(q.y)), fabsf(bf16_hi(q.y)))));
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(q.z)), fabsf(bf16_hi(q.z))),
+                           fmaxf(fabsf(bf16_lo(q.w)), fabsf(bf16_hi(q.w)))));
+      }
+      m = wave_max_dpp(m);
+      float* wmax = reinterpret_cast<float*>(smem);
+      if (lane == 0) wmax[wave] = m;
+      __syncthreads();
+      m = wave_max_dpp(wmax[lane & (kAlignWaves - 1)]);
+      const float s = scale_from_amax_bits(__float_as_uint(m));
+      if (tid == 0) a.sx_rows[blockIdx.x - 1] = s;
+      for (int64_t j = tid; j < h8; j += kAlignThreads) {
+        const uint4 q = a.x[base + j];
+        uint2 o;
+        o.x = e4m3_pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
+        o.y = e4m3_pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
+        a.qx[base + j] = o;
+      }
+      return;
+    }
     if (blockIdx.x > 0) {
       float m = 0.0f;
       for (int64_t base = 0; base < a.n8; base += kXBatch * kAlignThreads) {
@@ -106,8 +136,11 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
 
 template <bool FP8>
 hipError_t launch_vpl(const FrontArgs& a, int vpl, size_t lds, hipStream_t stream) {
-  // FP8: one workgroup per kXSlice 16-byte pieces of x, after workgroup 0
-  const unsigned nq = FP8 ? (unsigned)((a.n8 + kXSlice - 1) / kXSlice) : 0u;
+  // FP8: one workgroup per kXSlice 16-byte pieces of x, or per token row
+  // with per-row scales, after workgroup 0
+  const unsigned nq = !FP8 ? 0u
+                      : a.sx_rows ? (unsigned)a.T
+                                  : (unsigned)((a.n8 + kXSlice - 1) / kXSlice);
   const dim3 grid(1 + (nq > 0 ? nq : (FP8 ? 1u : 0u))), block(kAlignThreads);
   if (vpl <= 1) front_kernel<1, FP8><<<grid, block, lds, stream>>>(a);
   else if (vpl <= 2) front_kernel<2, FP8><<<grid, block, lds, stream>>>(a);
@@ -147,9 +180,9 @@ bool front_fits(int64_t T, int H, int K, bool fp8) {
 
 hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm, int32_t* ids,
                         float* wts, bool fp8, const void* x, int H, uint32_t* amax_x,
-                        uint32_t* amax_a, uint8_t* qx, int BM, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
-                        hipStream_t stream) {
+                        uint32_t* amax_a, uint8_t* qx, float* sx_rows, int BM,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                        int32_t* rank, hipStream_t stream) {
   FrontArgs a{};
   a.logits = logits;
   a.T = (int)T;
@@ -163,6 +196,7 @@ hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm
   a.amax_x = amax_x;
   a.amax_a = amax_a;
   a.qx = reinterpret_cast<uint2*>(qx);
+  a.sx_rows = sx_rows;
   a.out = AlignOut{sorted_ids, block_expert, num_post_pad, BM};
   a.rank = rank;
   const int vpl = (E + kWave - 1) / kWave;

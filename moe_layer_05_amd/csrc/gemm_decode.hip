@@ -334,8 +334,14 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
   }
 
   // ------------------------------------------------------------ epilogue
+  // Lane (g4, r16) holds rows 4*g4 + v of each 16-row weight tile for token
+  // column r16.  Per tensor: one scale for the whole block; per row: the
+  // weight row's scale times the activation row's.
   float scale = 1.0f;
-  if constexpr (FP8) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[e];
+  const bool rows = FP8 && p.row_scales;
+  const int64_t wrow0 = (int64_t)e * (MODE == kGateUp ? 2 * p.I : p.H);
+  if constexpr (FP8)
+    if (!rows) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[e];
 
   if constexpr (MODE == kGateUp) {
     float local_max = 0.0f;
@@ -344,15 +350,18 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
       if (s >= nsub) continue;
       const int32_t pair = blk[s * 16 + r16];
       if (pair >= p.P) continue;
+      const float sa = rows ? p.act_scale[pair / p.b_row_div] : 1.0f;
 #pragma unroll
       for (int cg = 0; cg < RA / 2; ++cg) {
         if (!a_ok[2 * cg]) continue;
         const int col = row0[2 * cg] + 4 * g4;
+        float sg[4] = {scale, scale, scale, scale}, su[4] = {scale, scale, scale, scale};
+        if (rows) row_scales4(p.w_scale + wrow0, col, p.I + col, sa, sg, su);
         float av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float gt = acc[2 * cg][s][v] * scale;
-          const float up = acc[2 * cg + 1][s][v] * scale;
+          const float gt = acc[2 * cg][s][v] * sg[v];
+          const float up = acc[2 * cg + 1][s][v] * su[v];
           av[v] = silu_fast(gt) * up;
           local_max = fmaxf(local_max, fabsf(av[v]));
         }
@@ -369,8 +378,10 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
       }
     }
     if constexpr (FP8) {
-      local_max = wave_max(local_max);
-      if (lane == 0 && local_max > 0.0f) amax_slot_max(p.a_amax, (uint32_t)unit, local_max);
+      if (!rows) {
+        local_max = wave_max(local_max);
+        if (lane == 0 && local_max > 0.0f) amax_slot_max(p.a_amax, (uint32_t)unit, local_max);
+      }
     }
   } else {
     const int64_t part = (int64_t)split * p.dw_split_stride;
@@ -379,13 +390,15 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
       if (s >= nsub) continue;
       const int32_t pair = blk[s * 16 + r16];
       if (pair >= p.P) continue;
-      const float sc = scale;
+      const float sa = rows ? p.act_scale[pair] : 1.0f;
 #pragma unroll
       for (int ra = 0; ra < RA; ++ra) {
         if (!a_ok[ra]) continue;
+        float sc[4] = {scale, scale, scale, scale};
+        if (rows) row_scales4(p.w_scale + wrow0, row0[ra] + 4 * g4, sa, sc);
         store_part4(p.dw, p.dw_bf16, part + (int64_t)pair * p.H + row0[ra] + 4 * g4,
-                    acc[ra][s][0] * sc, acc[ra][s][1] * sc, acc[ra][s][2] * sc,
-                    acc[ra][s][3] * sc);
+                    acc[ra][s][0] * sc[0], acc[ra][s][1] * sc[1], acc[ra][s][2] * sc[2],
+                    acc[ra][s][3] * sc[3]);
       }
     }
   }
@@ -400,7 +413,8 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
 // expert's weight scale -- also arrives by direct-to-LDS loads in the same
 // ordered stream, ahead of use, into small per-wave slots; no register load
 // whose wait would drain the stream sits on the path.  Rows may end in a
-// partial chunk (as in the one-wave-per-unit form).
+// partial chunk (as in the one-wave-per-unit form).  Per-tensor scales only:
+// the host launches the one-wave-per-unit form for per-row scales.
 //
 // Schedule, in steps t = k * cps + j (unit k, chunk j, cps chunks per unit):
 // during step t the wave consumes stage t % D, then issues the chunk of step
@@ -709,7 +723,9 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
   const int cps = (int)(nchunks / p.splits);
   const int lds = stream_lds(DS, RA + NSUB, cps > 0 ? cps : 1);
   const int64_t resident = (int64_t)num_cus * std::max(1, (160 * 1024) / lds);
-  const bool stream_ok = DS > 1 && nchunks % p.splits == 0 && cps >= 1 &&
+  // The persistent form carries one weight scale per unit in its metadata
+  // slots, so per-row scales take the classic form.
+  const bool stream_ok = !p.row_scales && DS > 1 && nchunks % p.splits == 0 && cps >= 1 &&
                          grid.x >= 2 * resident && grid.x < 8 * resident;
   if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, DC>(p, grid, stream);
   const unsigned g = (unsigned)std::min<int64_t>(grid.x, resident);

@@ -249,24 +249,32 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   };
 
   // ------------------------------------------------------------ epilogue
+  // Lane (g4, l16) holds weight rows 4*g4 + v of each 16-row sub-tile for
+  // token column l16; per-row scales as in the decode form.
+  const bool rows = FP8 && p.row_scales;
   auto epilogue = [&](const Tile& s) {
     float scale = 1.0f;
-    if constexpr (FP8) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[s.e];
+    const int64_t wrow0 = (int64_t)s.e * (MODE == kGateUp ? 2 * p.I : p.H);
+    if constexpr (FP8)
+      if (!rows) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[s.e];
     if constexpr (MODE == kGateUp) {
       float local_max = 0.0f;
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) {
         const int32_t pair = s.blk[64 * wn + 16 * bj + l16];
         if (pair >= p.P) continue;
+        const float sa = rows ? p.act_scale[pair / p.b_row_div] : 1.0f;
 #pragma unroll
         for (int ai = 0; ai < 4; ++ai) {
           const int col = s.n * 128 + 64 * wm + 16 * ai + 4 * g4;
           if (col >= p.I) continue;
+          float sg[4] = {scale, scale, scale, scale}, su[4] = {scale, scale, scale, scale};
+          if (rows) row_scales4(p.w_scale + wrow0, col, p.I + col, sa, sg, su);
           float av[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float gt = acc[ai][bj][v] * scale;
-            const float up = acc[ai + 4][bj][v] * scale;
+            const float gt = acc[ai][bj][v] * sg[v];
+            const float up = acc[ai + 4][bj][v] * su[v];
             av[v] = silu_fast(gt) * up;
             local_max = fmaxf(local_max, fabsf(av[v]));
           }
@@ -283,22 +291,26 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
         }
       }
       if constexpr (FP8) {
-        local_max = wave_max(local_max);
-        if (lane == 0 && local_max > 0.0f)
-          amax_slot_max(p.a_amax, (uint32_t)(blockIdx.x * kWaves + wave), local_max);
+        if (!rows) {
+          local_max = wave_max(local_max);
+          if (lane == 0 && local_max > 0.0f)
+            amax_slot_max(p.a_amax, (uint32_t)(blockIdx.x * kWaves + wave), local_max);
+        }
       }
     } else {
 #pragma unroll
       for (int bj = 0; bj < 4; ++bj) {
         const int32_t pair = s.blk[64 * wn + 16 * bj + l16];
         if (pair >= p.P) continue;
-        const float sc = scale;
+        const float sa = rows ? p.act_scale[pair] : 1.0f;
 #pragma unroll
         for (int ai = 0; ai < 8; ++ai) {
           const int h = s.n * kTM + 128 * wm + 16 * ai + 4 * g4;
           if (h >= p.H) continue;
-          store_part4(p.dw, p.dw_bf16, (int64_t)pair * p.H + h, acc[ai][bj][0] * sc,
-                      acc[ai][bj][1] * sc, acc[ai][bj][2] * sc, acc[ai][bj][3] * sc);
+          float sc[4] = {scale, scale, scale, scale};
+          if (rows) row_scales4(p.w_scale + wrow0, h, sa, sc);
+          store_part4(p.dw, p.dw_bf16, (int64_t)pair * p.H + h, acc[ai][bj][0] * sc[0],
+                      acc[ai][bj][1] * sc[1], acc[ai][bj][2] * sc[2], acc[ai][bj][3] * sc[3]);
         }
       }
     }

@@ -24,8 +24,13 @@ struct GemmParams {
   int P;                       // pairs (= sentinel)
   int groups;                  // row groups per block (one wave each)
   int splits;                  // parts of the reduction dimension
-  const float* w_scale;        // [E] (FP8) or nullptr
-  const uint32_t* act_amax;    // final amax bits of B's quantisation (FP8) or nullptr
+  const float* w_scale;        // [E] (FP8), [E][rows] with row_scales, or nullptr
+  const uint32_t* act_amax;    // final amax bits of B's quantisation (FP8 per tensor) or nullptr
+  // FP8 with one scale per weight row and per activation row: w_scale holds
+  // one scale per output row of each expert (2I for gate/up, H for down) and
+  // act_scale one per row of B; act_amax and a_amax are unused.
+  int row_scales;
+  const float* act_scale;      // [rows of B] float32, with row_scales
   // gate/up
   void* a_out;                 // [P][I] float32 (FP8 path) or bfloat16
   uint32_t* a_amax;            // amax block (slots) of a (FP8) or nullptr
@@ -53,14 +58,15 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
                         hipStream_t stream);
 
 // a1 + a0 + a2 by one workgroup for small batches (front_fits): routing,
-// (FP8) the codes of x with the final amax word, the amax slots of a cleared,
-// and the align layout with block size BM.
+// (FP8) the codes of x with the final amax word and the amax slots of a
+// cleared -- or, when sx_rows is set, the codes of x with one scale per token
+// row, written to sx_rows -- and the align layout with block size BM.
 bool front_fits(int64_t T, int H, int K, bool fp8);
 hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm, int32_t* ids,
                         float* wts, bool fp8, const void* x, int H, uint32_t* amax_x,
-                        uint32_t* amax_a, uint8_t* qx, int BM, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
-                        hipStream_t stream);
+                        uint32_t* amax_a, uint8_t* qx, float* sx_rows, int BM,
+                        int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
+                        int32_t* rank, hipStream_t stream);
 
 // Two layouts at once (prefill), by three multi-workgroup launches: experts
 // with >= thr pairs in blocks of BM_big, the others in blocks of BM_small;
@@ -77,6 +83,10 @@ hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cu
                             hipStream_t stream);
 hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
                              float* scale_out, int num_cus, hipStream_t stream);
+// Per-row E4M3: scales[r] = amax|row r| / 448 (1 when 0), codes = E4M3(v /
+// scales[r]); rows of C values (C % 8 == 0), bfloat16 or float32.
+hipError_t launch_quant_rows(const void* src, bool bf16, int64_t rows, int C, uint8_t* codes,
+                             float* scales, int num_cus, hipStream_t stream);
 hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream);
 

@@ -1,4 +1,4 @@
-// a0 and the intermediate quantisation of a4: per-tensor E4M3.
+// a0 and the intermediate quantisation of a4: E4M3 per tensor, or per row.
 //
 // FP8 E4M3 (4 exponent, 3 mantissa bits) with one scale per tensor:
 // kongchang.com page, FP8 explainer under "Triton Backend Routing"; aib.vote
@@ -10,6 +10,12 @@
 // IEEE division, so the codes are exactly those of a float32 reference; its
 // first thread also stores the final amax for later kernels.  Both kernels
 // stream with 16-byte loads and are bandwidth-bound.
+//
+// The per-row form (one scale per token row of x, per pair row of the
+// intermediate) carries the kongchang.com page's concern in "Triton Backend
+// Routing: A Practical Path to FP8 Quantization" -- value distributions
+// differ, so one uniform scale loses precision -- from experts down to rows:
+// a row's own scale keeps its small values out of the E4M3 subnormal range.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -72,6 +78,57 @@ __global__ __launch_bounds__(256) void quant_f32_kernel(const float4* __restrict
   }
 }
 
+// Per-row form: one wave per row (grid-stride over rows).  The wave reduces
+// the row's amax from 16-byte loads, forms s = amax / 448 with the same
+// arithmetic as the per-tensor form, and writes the codes on a second read of
+// the row (from cache: a row is at most a few tens of KB).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* src, int64_t j, float (&v)[8]) {
+  if constexpr (BF16) {
+    const uint4 q = static_cast<const uint4*>(src)[j];
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+  } else {
+    const float4 p = static_cast<const float4*>(src)[2 * j];
+    const float4 q = static_cast<const float4*>(src)[2 * j + 1];
+    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+    v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src,
+                                                         int64_t rows, int c8,
+                                                         uint2* __restrict__ codes,
+                                                         float* __restrict__ scales) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; r < rows;
+       r += nw) {
+    const int64_t base = r * c8;
+    float m = 0.0f;
+#pragma unroll 4
+    for (int j = lane; j < c8; j += kWave) {
+      float v[8];
+      load8<BF16>(src, base + j, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+    m = wave_max_dpp(m);
+    const float s = scale_from_amax_bits(__float_as_uint(m));
+    if (lane == 0) scales[r] = s;
+#pragma unroll 4
+    for (int j = lane; j < c8; j += kWave) {
+      float v[8];
+      load8<BF16>(src, base + j, v);
+      uint2 o;
+      o.x = e4m3_pack4(v[0], v[1], v[2], v[3], s);
+      o.y = e4m3_pack4(v[4], v[5], v[6], v[7], s);
+      codes[base + j] = o;
+    }
+  }
+}
+
 // Clears the slots of n consecutive amax blocks.
 __global__ void zero_amax_kernel(uint32_t* p, int nblocks) {
   for (int t = threadIdx.x; t < nblocks * kAmaxSlots; t += blockDim.x) p[amax_zero_index(t)] = 0u;
@@ -90,7 +147,9 @@ hipError_t prepare_quant_kernels() {
   const void* fns[] = {reinterpret_cast<const void*>(&amax_bf16_kernel),
                        reinterpret_cast<const void*>(&quant_bf16_kernel),
                        reinterpret_cast<const void*>(&quant_f32_kernel),
-                       reinterpret_cast<const void*>(&zero_amax_kernel)};
+                       reinterpret_cast<const void*>(&zero_amax_kernel),
+                       reinterpret_cast<const void*>(&quant_rows_kernel<true>),
+                       reinterpret_cast<const void*>(&quant_rows_kernel<false>)};
   for (const void* f : fns) {
     const hipError_t e = prepare_kernel(f, 0);
     if (e != hipSuccess) return e;
@@ -124,6 +183,20 @@ hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* 
   const int64_t n8 = n / 8;
   quant_f32_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
       reinterpret_cast<const float4*>(a), n8, amax, reinterpret_cast<uint2*>(codes));
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* src, bool bf16, int64_t rows, int C, uint8_t* codes,
+                             float* scales, int num_cus, hipStream_t stream) {
+  int64_t blocks = (rows + 3) / 4;                 // 4 waves (rows) per block
+  if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
+  const unsigned grid = (unsigned)(blocks > 0 ? blocks : 1);
+  if (bf16)
+    quant_rows_kernel<true><<<grid, 256, 0, stream>>>(src, rows, C / 8,
+                                                      reinterpret_cast<uint2*>(codes), scales);
+  else
+    quant_rows_kernel<false><<<grid, 256, 0, stream>>>(src, rows, C / 8,
+                                                       reinterpret_cast<uint2*>(codes), scales);
   return hipGetLastError();
 }
 

@@ -105,9 +105,10 @@ def quantize(v, scale=None):
 def quantize_rows(v):
     """(codes, scales) of the E4M3 quantisation of each row with its own scale.
 
-    The finer granularity the kongchang.com page motivates in "Triton Backend
-    Routing: A Practical Path to FP8 Quantization" (experts, and channels or
-    tokens within them, differ in their numerical distributions): row r gets
+    Finer granularity, read from the kongchang.com page, "Triton Backend
+    Routing: A Practical Path to FP8 Quantization" (numerical distributions
+    differ, so one uniform scale loses precision; here carried from experts
+    down to weight channels and activation rows): row r gets
     s_r = amax|v_r| / 448 (``per_tensor_scale`` of the row alone) and codes
     encode(v_r / s_r).  ``v`` is [R, C]; returns codes [R, C] uint8 and scales
     [R] float32.

@@ -194,7 +194,8 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
 
     Returns out [len(tokens), H] float32 holding bfloat16 values; with
     ``return_parts`` also a dict with y (before rounding), ids, weights and,
-    in FP8 mode, the activation scales.
+    in FP8 mode, the activation scales and the intermediate rows before their
+    quantisation (a_f32, one row per (t, k) in a_pairs).
 
     In FP8 mode the intermediate scale needs every routed pair, so gate/up runs
     for all pairs; the down projection and the combine run for ``tokens`` only.
@@ -247,6 +248,8 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
         for r, kk in enumerate(keys):
             a[kk] = ah[r].astype(dtype)
         parts["s_a"] = s_a
+        parts["a_pairs"] = keys              # (t, k) of each row of a_f32 / s_a
+        parts["a_f32"] = amat                # the values that were quantised
 
     # down projection and routing-weighted combine
     def down_of(e):

@@ -51,7 +51,7 @@ def test_struct_layout_matches_c():
 int main(void) {
   printf("%zu", sizeof(moe_fused_args));
 #define F(n) printf(" %zu", offsetof(moe_fused_args, n));
-  F(wdtype) F(T) F(H) F(I) F(E) F(K) F(renormalize) F(x) F(router_logits) F(w13) F(w2)
+  F(wdtype) F(fp8_scales) F(T) F(H) F(I) F(E) F(K) F(renormalize) F(x) F(router_logits) F(w13) F(w2)
   F(w13_scale) F(w2_scale) F(out) F(topk_ids_out) F(topk_weights_out) F(workspace)
   F(workspace_bytes)
   return 0;
@@ -112,6 +112,15 @@ def test_act_quant_validation(L):
     assert L.moe_act_quant_fp8(p, -8, p, p, p, 256, None) == SHAPE
 
 
+def test_act_quant_rows_validation(L):
+    p = ctypes.c_void_p(256)
+    assert L.moe_act_quant_fp8_rows(p, 4, 12, p, p, None) == UNSUP             # cols % 8
+    assert L.moe_act_quant_fp8_rows(ctypes.c_void_p(258), 4, 16, p, p, None) == UNSUP
+    assert L.moe_act_quant_fp8_rows(p, 4, 16, p, None, None) == NULL
+    assert L.moe_act_quant_fp8_rows(p, -1, 16, p, p, None) == SHAPE
+    assert L.moe_act_quant_fp8_rows(None, 0, 16, None, None, None) == OK      # no rows
+
+
 def _args(**kw):
     a = binding.FusedArgs()
     a.wdtype, a.T, a.H, a.I, a.E, a.K, a.renormalize = 1, 8, 256, 64, 16, 4, 1
@@ -141,6 +150,10 @@ def test_fused_validation(L):
     assert _fwd(L, w13_scale=None) == NULL          # fp8 needs scales
     assert _fwd(L, out=4097) == UNSUP               # misaligned
     assert _fwd(L, workspace_bytes=16) == WS
+    assert _fwd(L, fp8_scales=2) == UNSUP           # unknown scale mode
+    assert _fwd(L, fp8_scales=1, w2_scale=4100) == UNSUP   # row scales: 16-byte aligned
+    assert _fwd(L, wdtype=0, fp8_scales=9, w13_scale=None, w2_scale=None,
+                workspace_bytes=16) == WS           # bf16 ignores the scale mode
     assert _fwd(L, T=0, x=None, out=None) == OK     # empty batch: no-op
 
 
@@ -160,5 +173,11 @@ def test_fused_block_m_and_workspace(L):
     assert n1 > 8 * 4 * (256 * 4)                    # at least the pair outputs
     a.T = 16
     assert L.moe_fused_workspace_bytes(ctypes.byref(a)) > n1
+    a.fp8_scales = 1                                 # per-row scales of x and a
+    assert L.moe_fused_workspace_bytes(ctypes.byref(a)) >= \
+        L.moe_fused_workspace_bytes(ctypes.byref(_args(T=16))) + (16 + 16 * 4) * 4
+    a.fp8_scales = 5
+    assert L.moe_fused_workspace_bytes(ctypes.byref(a)) == 0
+    a.fp8_scales = 0
     a.K = 99
     assert L.moe_fused_workspace_bytes(ctypes.byref(a)) == 0

@@ -1,6 +1,7 @@
 """GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
 
-Bars: routing ids, the aligned layout and E4M3 activation codes bit-exact;
+Bars: routing ids, the aligned layout and E4M3 activation codes (and their
+per-row scales) bit-exact;
 routing weights within 1e-6 absolute; the layer output within 1e-2 relative,
 measured as max|out - ref| / max|ref| over the compared tokens (bfloat16 and
 FP8 outputs against the float64 oracle).  Every call goes through the C ABI.
@@ -142,17 +143,41 @@ def test_act_quant_zeros():
     _check_quant(torch.zeros(4, 64, dtype=torch.bfloat16))
 
 
+@pytest.mark.parametrize("shape", [(1, 4096), (5, 7168), (64, 7168), (4096, 7168), (3, 8),
+                                   (300, 1040)])
+def test_act_quant_rows_bit_exact(shape):
+    """Per-row codes and scales against the oracle's row quantiser; rows of
+    very different magnitude (including an all-zero row and one whose values
+    fall into the E4M3 subnormal range of a shared scale)."""
+    g = torch.Generator().manual_seed(shape[0] * 7 + shape[1])
+    mag = torch.pow(10.0, torch.empty(shape[0], 1).uniform_(-6, 4, generator=g))
+    x = torch.randn(*shape, generator=g) * mag
+    x[shape[0] // 2] = 0.0
+    x = x.to(torch.bfloat16)
+    say("act_quant rows", shape)
+    codes, scales = mm.act_quant_fp8_rows(x.to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = ofp8.quantize_rows(np_f32(x))
+    assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, rc), int((got != rc).sum())
+
+
 # ------------------------------------------------------------------ fused layer
 
 _WCACHE = {}
 
 
 def _weights(cfg, wdtype, gen_dev):
+    """Weights of cfg; wdtype "fp8row" is E4M3 with one scale per weight row
+    (and the layer then takes one scale per activation row)."""
     key = (cfg.H, cfg.I, cfg.E, cfg.K, cfg.weight_std, wdtype, gen_dev)
     if key not in _WCACHE:
         if len(_WCACHE) > 2:
             _WCACHE.clear()
-        w = workloads.make_weights(cfg, seed=0, device=gen_dev, wdtype=wdtype)
+        rows = wdtype == "fp8row"
+        w = workloads.make_weights(cfg, seed=0, device=gen_dev, wdtype="fp8" if rows else wdtype,
+                                   scales="row" if rows else "tensor")
         _WCACHE[key] = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
     return _WCACHE[key]
 
@@ -168,6 +193,7 @@ def run_case(cfg, T, wdtype, tokens=None, logits_kind=None, gen_dev="cpu", seed=
     out, ids, _ = m(tk["x"], tk["logits"], return_topk=True)
     torch.cuda.synchronize()
     ref, parts = omoe.moe_forward(K=cfg.K, tokens=tokens, return_parts=True, workers=WORKERS,
+                                  act_scales="row" if wdtype == "fp8row" else "tensor",
                                   **oracle_inputs(w, tk))
     assert np.array_equal(ids.cpu().numpy(), parts["ids"])
     got = np_f32(out)
@@ -176,20 +202,68 @@ def run_case(cfg, T, wdtype, tokens=None, logits_kind=None, gen_dev="cpu", seed=
     err = rel_err(got, ref)
     assert np.isfinite(got).all()
     say("  rel err", err)
-    assert err <= TOL, err
+    if wdtype == "fp8row":
+        sel = np.arange(T) if tokens is None else np.asarray(tokens)
+        allow = near_tie_allowance(parts, w, cfg, sel)
+        excess = np.abs(got.astype(np.float64) - ref) - TOL * np.abs(ref).max()
+        say("  near-tie allowance used at", int((excess > 0).sum()), "elements; max allowance",
+            float(allow.max() / max(np.abs(ref).max(), 1e-30)))
+        assert (excess <= allow).all(), float((excess - allow).max())
+    else:
+        assert err <= TOL, err
     return err
+
+
+# Per-row scales put the largest intermediate values of every pair in E4M3's
+# top binade (steps of 32 code units), so one code that rounds the other way
+# moves the output by up to about 1% of its maximum at small I.  Such a code
+# is as valid as the oracle's when the float64 value lies within the GPU's
+# arithmetic error of a rounding midpoint: the fp8 matrix instruction sums the
+# products of one instruction with about 16 bits below the largest of them
+# (a one-wave check of the builtin: 448*448 - 448*448 + 1 sums to 0), and the
+# GPU's intermediate was measured within 5e-5 of the float64 one relative to
+# its row amax (0.021 code units at 448).  Codes whose float64 value lies
+# within NEAR_TIE * 448 code units of a midpoint may round either way; the
+# parity bar for per-row scales is 1e-2 of max|ref| plus the largest output
+# change those codes can cause (a 5% error on one token still fails it).
+NEAR_TIE = 2.0 ** -13
+
+
+def near_tie_allowance(parts, w, cfg, tokens):
+    """[len(tokens), H] bound on the output change that near-tie intermediate
+    codes can cause by rounding to the other neighbour (per-row scales)."""
+    grid = np.unique(np.abs(ofp8.decode(np.arange(256, dtype=np.uint8))))
+    grid = grid[np.isfinite(grid)]
+    row_of = {int(t): r for r, t in enumerate(tokens)}
+    allow = np.zeros((len(tokens), cfg.H))
+    wts = parts["weights"]
+    for r, (t, k) in enumerate(parts["a_pairs"]):
+        if t not in row_of:
+            continue
+        s = np.float64(parts["s_a"][r])
+        v = np.abs(parts["a_f32"][r].astype(np.float64)) / s
+        j = np.clip(np.searchsorted(grid, v), 1, grid.size - 1)
+        lo, hi = grid[j - 1], grid[j]
+        near = np.abs(v - (lo + hi) / 2) <= NEAR_TIE * 448.0
+        if not near.any():
+            continue
+        e = int(parts["ids"][t, k])
+        w2 = ofp8.decode(np_u8(w["w2"][e])) * np_f32(w["w2_scale"][e]).astype(np.float64)[:, None]
+        step = (hi - lo)[near] * s
+        allow[row_of[t]] += abs(wts[t, k]) * (np.abs(w2[:, near]) @ step)
+    return allow
 
 
 TINY = workloads.CONFIGS["tiny"]
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
 @pytest.mark.parametrize("T", [1, 4, 5, 16, 17, 33, 64, 100, 300])
 def test_fused_tiny(T, wdtype):
     run_case(TINY, T, wdtype)
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
 @pytest.mark.parametrize("over", [
     dict(H=144, I=48, E=6, K=3),         # ragged chunk tails in both GEMMs
     dict(H=272, I=80, E=5, K=5),         # K = E
@@ -202,7 +276,7 @@ def test_fused_shapes(over, wdtype):
         run_case(cfg, T, wdtype)
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
 def test_fused_tie_heavy_routing(wdtype):
     run_case(TINY, 50, wdtype, logits_kind="ties")
 
@@ -222,25 +296,28 @@ def test_fused_bf16_decode(T):
     run_case(workloads.CONFIGS["bf16_decode"], T, "bf16", gen_dev=DEV)
 
 
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8row"])
 @pytest.mark.parametrize("T", [1, 8, 32, 64])
-def test_fused_fp8_decode(T):
-    run_case(workloads.CONFIGS["fp8_decode"], T, "fp8", gen_dev=DEV)
+def test_fused_fp8_decode(T, wdtype):
+    run_case(workloads.CONFIGS["fp8_decode"], T, wdtype, gen_dev=DEV)
 
 
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8row"])
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
-def test_fused_fp8_tp8_slice(T):
-    run_case(workloads.CONFIGS["fp8_tp8_slice"], T, "fp8", gen_dev=DEV)
+def test_fused_fp8_tp8_slice(T, wdtype):
+    run_case(workloads.CONFIGS["fp8_tp8_slice"], T, wdtype, gen_dev=DEV)
 
 
-def test_fused_fp8_prefill_zipf_sampled():
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8row"])
+def test_fused_fp8_prefill_zipf_sampled(wdtype):
     cfg = workloads.CONFIGS["fp8_prefill_zipf"]
     tokens = np.random.default_rng(0).choice(4096, 24, replace=False)
-    run_case(cfg, 4096, "fp8", tokens=np.sort(tokens), gen_dev=DEV)
+    run_case(cfg, 4096, wdtype, tokens=np.sort(tokens), gen_dev=DEV)
 
 
 # ------------------------------------------------------------------ determinism
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
 @pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 7),   # front launch (T <= 16)
     (dict(H=2048, I=1040, E=16, K=4), 40),  # router, act quant and align launches
@@ -273,7 +350,7 @@ def test_fused_graph_replay_matches_eager(over, T, wdtype):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
 @pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 7),   # row tails in both products
     (dict(H=144, I=48, E=6, K=3), 40),
@@ -295,7 +372,7 @@ def test_fused_run_to_run_bit_identical(over, T, wdtype):
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
 @pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 512),   # tiled experts + small ones, column and row tails
     (dict(H=1152, I=320, E=32, K=6), 700),
