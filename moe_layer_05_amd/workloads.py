@@ -68,6 +68,8 @@ CONFIGS = {
 }
 
 FP8_MAX = 448.0
+E5M2_MAX = 57344.0
+_FP8_TYPES = {"e4m3": (torch.float8_e4m3fn, FP8_MAX), "e5m2": (torch.float8_e5m2, E5M2_MAX)}
 _ROLE_WEIGHTS = 1
 _ROLE_TOKENS = 2
 
@@ -84,32 +86,36 @@ def _std(cfg, fan_in):
     return float(cfg.weight_std)
 
 
-def fp8_codes_per_expert(w):
+def fp8_codes_per_expert(w, fmt="e4m3"):
     """(uint8 codes, float32 scales) of float32 weights [E, R, C]; one scale per
-    expert tensor, amax / 448, via torch's float8_e4m3fn cast."""
+    expert tensor, amax / max, via torch's float8 cast (e4m3fn or e5m2)."""
+    dt, vmax = _FP8_TYPES[fmt]
     E = w.shape[0]
     amax = w.abs().reshape(E, -1).amax(dim=1).to(torch.float32)
-    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
-    q = (w / scale.view(E, 1, 1)).clamp_(-FP8_MAX, FP8_MAX)
-    return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
+    scale = torch.where(amax > 0, amax / vmax, torch.ones_like(amax))
+    q = (w / scale.view(E, 1, 1)).clamp_(-vmax, vmax)
+    return q.to(dt).view(torch.uint8), scale
 
 
-def fp8_codes_per_row(w):
+def fp8_codes_per_row(w, fmt="e4m3"):
     """(uint8 codes, float32 scales [E, R]) of float32 weights [E, R, C]; one
-    scale per expert row (output channel), amax / 448, via torch's
-    float8_e4m3fn cast."""
+    scale per expert row (output channel), amax / max, via torch's float8
+    cast."""
+    dt, vmax = _FP8_TYPES[fmt]
     amax = w.abs().amax(dim=2).to(torch.float32)
-    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
-    q = (w / scale.unsqueeze(2)).clamp_(-FP8_MAX, FP8_MAX)
-    return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
+    scale = torch.where(amax > 0, amax / vmax, torch.ones_like(amax))
+    q = (w / scale.unsqueeze(2)).clamp_(-vmax, vmax)
+    return q.to(dt).view(torch.uint8), scale
 
 
-def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8, scales="tensor"):
+def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8, scales="tensor",
+                 fp8_format="e4m3"):
     """Expert weights of ``cfg``.
 
     Returns a dict with w13 [E, 2I, H] and w2 [E, H, I] (float32, bfloat16 or
     uint8 E4M3 codes) and, for E4M3, w13_scale and w2_scale: [E] float32, or
-    with ``scales="row"`` one per output row, [E, 2I] and [E, H].
+    with ``scales="row"`` one per output row, [E, 2I] and [E, H]; the codes
+    are E4M3, or E5M2 with ``fp8_format="e5m2"`` (scale amax / 57344).
     ``wdtype`` overrides the configuration's storage type (the tiny float32
     case is also run as bfloat16 and as E4M3).  Experts are drawn ``chunk`` at a
     time to bound the float32 staging memory; the stream order is w13 of the
@@ -132,8 +138,8 @@ def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8, scales="tensor
         a = torch.randn(e1 - e0, 2 * I, H, generator=g, device=device) * s13
         b = torch.randn(e1 - e0, H, I, generator=g, device=device) * s2
         if wdtype == "fp8":
-            w13[e0:e1], sc13[e0:e1] = quant(a)
-            w2[e0:e1], sc2[e0:e1] = quant(b)
+            w13[e0:e1], sc13[e0:e1] = quant(a, fp8_format)
+            w2[e0:e1], sc2[e0:e1] = quant(b, fp8_format)
         else:
             w13[e0:e1] = a.to(store)
             w2[e0:e1] = b.to(store)
@@ -142,6 +148,7 @@ def make_weights(cfg, seed=0, device="cpu", wdtype=None, chunk=8, scales="tensor
     if wdtype == "fp8":
         out["w13_scale"] = sc13
         out["w2_scale"] = sc2
+        out["fp8_format"] = fp8_format
     return out
 
 

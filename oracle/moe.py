@@ -125,23 +125,24 @@ def align(ids, E, block_m):
 # a0: activation quantisation (FP8 mode)
 # --------------------------------------------------------------------------
 
-def act_quant(x, scales="tensor"):
-    """E4M3 quantisation of the activations: (codes uint8, scale).
+def act_quant(x, scales="tensor", fmt="e4m3"):
+    """FP8 quantisation of the activations: (codes uint8, scale).
 
     scales == "tensor": one scale for the whole [T, H] tensor (float32).
     scales == "row":    one scale per token row, [T] float32.
+    fmt: "e4m3" or "e5m2".
     """
     x32 = np.asarray(x, dtype=np.float32)
     if scales == "row":
-        return _fp8.quantize_rows(x32)
-    return _fp8.quantize(x32)
+        return _fp8.quantize_rows(x32, fmt)
+    return _fp8.quantize(x32, fmt=fmt)
 
 
-def _dequant(codes, scale, scales):
+def _dequant(codes, scale, scales, fmt="e4m3"):
     """codes times the tensor scale, or times each row's scale."""
     if scales == "row":
-        return _fp8.decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
-    return _fp8.decode(codes) * np.float64(scale)
+        return _fp8.decode(codes, fmt) * np.asarray(scale, dtype=np.float64)[:, None]
+    return _fp8.decode(codes, fmt) * np.float64(scale)
 
 
 # --------------------------------------------------------------------------
@@ -153,7 +154,7 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def _weight(wt, e, scale, fp8_mode, dtype):
+def _weight(wt, e, scale, fp8_mode, dtype, fmt="e4m3"):
     """Expert weight matrix in ``dtype``: code * scale (FP8) or the value.
 
     ``scale[e]`` is the expert tensor's scale, or an array with one scale per
@@ -162,8 +163,8 @@ def _weight(wt, e, scale, fp8_mode, dtype):
     if fp8_mode:
         se = np.asarray(scale[e], dtype=np.float64)
         if se.ndim == 1:
-            return (_fp8.decode(m) * se[:, None]).astype(dtype)
-        return (_fp8.decode(m) * np.float64(se)).astype(dtype)
+            return (_fp8.decode(m, fmt) * se[:, None]).astype(dtype)
+        return (_fp8.decode(m, fmt) * np.float64(se)).astype(dtype)
     return m.astype(dtype)
 
 
@@ -176,7 +177,8 @@ def _gate_up(xh, W13, I):
 
 def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
                 w2_scale=None, renormalize=True, dtype=np.float64,
-                tokens=None, return_parts=False, workers=1, act_scales="tensor"):
+                tokens=None, return_parts=False, workers=1, act_scales="tensor",
+                fp8_format="e4m3"):
     """The layer output for the tokens in ``tokens`` (all by default).
 
     x       [T, H] float values (the bfloat16 activations as float32).
@@ -189,6 +191,8 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     act_scales  "tensor": one scale for x and one for the intermediate a over
             all routed pairs; "row": one per token row of x and one per pair
             row of a (FP8 only).
+    fp8_format  "e4m3" or "e5m2": the code format of the weights, x and a
+            (FP8 only).
     dtype   arithmetic precision of the products (float64 by default).
     workers experts evaluated concurrently (same arithmetic, less wall time).
 
@@ -209,9 +213,10 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     tokens = np.asarray(tokens, dtype=np.int64)
     parts = {"ids": ids, "weights": wts}
 
+    fmt = fp8_format
     if fp8_mode:
-        qx, s_x = act_quant(x32, act_scales)
-        xh = _dequant(qx, s_x, act_scales).astype(dtype)
+        qx, s_x = act_quant(x32, act_scales, fmt)
+        xh = _dequant(qx, s_x, act_scales, fmt).astype(dtype)
         parts["s_x"] = s_x
     else:
         xh = x32.astype(dtype)
@@ -231,7 +236,7 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
             tk = tk[want[tk[:, 0]]]
         if tk.size == 0:
             return tk, None
-        W13 = _weight(w13, e, w13_scale, fp8_mode, dtype)
+        W13 = _weight(w13, e, w13_scale, fp8_mode, dtype, fmt)
         I = W13.shape[0] // 2
         return tk, _gate_up(xh[tk[:, 0]], W13, I)
 
@@ -243,8 +248,8 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     if fp8_mode and a:
         keys = sorted(a)
         amat = np.stack([a[kk] for kk in keys]).astype(np.float32)
-        qa, s_a = act_quant(amat, act_scales)
-        ah = _dequant(qa, s_a, act_scales)
+        qa, s_a = act_quant(amat, act_scales, fmt)
+        ah = _dequant(qa, s_a, act_scales, fmt)
         for r, kk in enumerate(keys):
             a[kk] = ah[r].astype(dtype)
         parts["s_a"] = s_a
@@ -257,7 +262,7 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
               if want[int(t)]]
         if not tk:
             return tk, None
-        W2 = _weight(w2, e, w2_scale, fp8_mode, dtype)
+        W2 = _weight(w2, e, w2_scale, fp8_mode, dtype, fmt)
         A = np.stack([a[p] for p in tk]).astype(dtype)
         return tk, A @ W2.T
 
@@ -275,7 +280,8 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
 
 
 def moe_dense(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
-              w2_scale=None, renormalize=True, dtype=np.float64, act_scales="tensor"):
+              w2_scale=None, renormalize=True, dtype=np.float64, act_scales="tensor",
+              fp8_format="e4m3"):
     """The same layer written as "run every expert on every token, mask".
 
     y_t = sum_e M[t, e] * expert_e(x_t), with M[t, e] the routing weight of e
@@ -294,29 +300,30 @@ def moe_dense(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
         for k in range(K):
             M[t, ids[t, k]] = wts[t, k]
             routed[t, ids[t, k]] = True
+    fmt = fp8_format
     if fp8_mode:
-        qx, s_x = act_quant(x32, act_scales)
-        xh = _dequant(qx, s_x, act_scales).astype(dtype)
+        qx, s_x = act_quant(x32, act_scales, fmt)
+        xh = _dequant(qx, s_x, act_scales, fmt).astype(dtype)
     else:
         xh = x32.astype(dtype)
     A = []
     for e in range(E):
-        W13 = _weight(w13, e, w13_scale, fp8_mode, dtype)
+        W13 = _weight(w13, e, w13_scale, fp8_mode, dtype, fmt)
         I = W13.shape[0] // 2
         A.append(_gate_up(xh, W13, I))       # [T, I] for every token
     A = np.stack(A, axis=1)                  # [T, E, I]
     if fp8_mode and act_scales == "row":
         # every (token, expert) row on its own scale; unrouted rows are masked
         flat = A.reshape(T * E, -1).astype(np.float32)
-        q, s_rows = _fp8.quantize_rows(flat)
-        A = (_fp8.decode(q) * s_rows.astype(np.float64)[:, None]).reshape(A.shape)
+        q, s_rows = _fp8.quantize_rows(flat, fmt)
+        A = (_fp8.decode(q, fmt) * s_rows.astype(np.float64)[:, None]).reshape(A.shape)
     elif fp8_mode:
         amax_src = A[routed].astype(np.float32)
-        s_a = _fp8.per_tensor_scale(amax_src)
-        q, _ = _fp8.quantize(A.astype(np.float32), scale=s_a)
-        A = _fp8.decode(q) * np.float64(s_a)
+        s_a = _fp8.per_tensor_scale(amax_src, fmt)
+        q, _ = _fp8.quantize(A.astype(np.float32), scale=s_a, fmt=fmt)
+        A = _fp8.decode(q, fmt) * np.float64(s_a)
     y = np.zeros((T, H))
     for e in range(E):
-        W2 = _weight(w2, e, w2_scale, fp8_mode, dtype)
+        W2 = _weight(w2, e, w2_scale, fp8_mode, dtype, fmt)
         y += M[:, e:e + 1] * (A[:, e, :].astype(dtype) @ W2.T)
     return y

@@ -48,6 +48,7 @@ def oracle_inputs(weights, tokens):
     if fp8:
         kw["w13_scale"] = np_f32(weights["w13_scale"])
         kw["w2_scale"] = np_f32(weights["w2_scale"])
+        kw["fp8_format"] = weights.get("fp8_format", "e4m3")
     return kw
 
 

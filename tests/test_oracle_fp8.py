@@ -154,3 +154,101 @@ def test_bf16_round_matches_torch():
 def test_encode_rejects_nan(bad):
     with pytest.raises(ValueError):
         fp8.encode(np.array([bad]))
+
+
+# ------------------------------------------------------------------ E5M2
+
+def _closed_form_e5m2(code):
+    """E5M2 value of a code as an exact Fraction; 'inf' / None for inf / NaN."""
+    s, e, m = code >> 7, (code >> 2) & 0x1F, code & 3
+    if e == 31:
+        return ("-inf" if s else "inf") if m == 0 else None
+    if e == 0:
+        mag = Fraction(m, 1 << 16)
+    else:
+        mag = (1 + Fraction(m, 4)) * Fraction(2) ** (e - 15)
+    return -mag if s else mag
+
+
+def test_e5m2_decode_table_closed_form():
+    tab = fp8.decode_table("e5m2")
+    for c in range(256):
+        v = _closed_form_e5m2(c)
+        if v is None:
+            assert np.isnan(tab[c])
+        elif isinstance(v, str):
+            assert tab[c] == (-np.inf if v == "-inf" else np.inf)
+        else:
+            assert Fraction(tab[c]) == v, hex(c)
+    assert tab[0x7B] == 57344.0 and tab[0xFB] == -57344.0
+    assert tab[0x01] == 2.0 ** -16 and tab[0x04] == 2.0 ** -14 and tab[0x3C] == 1.0
+
+
+def test_e5m2_decode_matches_torch_float8():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+    tab = fp8.decode_table("e5m2")
+    assert np.array_equal(np.isnan(ref), np.isnan(tab))
+    fin = ~np.isnan(tab)
+    assert np.array_equal(tab[fin], ref[fin])
+
+
+def _brute_force_e5m2(v):
+    """Nearest finite E5M2 value by search; ties -> even code; saturating."""
+    tab = fp8.decode_table("e5m2")
+    pos_codes = np.arange(0x7C)                   # 0x00 .. 0x7B: +0 .. 57344
+    mags = tab[pos_codes]
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 57344.0)
+    d = np.abs(a[:, None] - mags[None, :])
+    cand = d == d.min(axis=1, keepdims=True)
+    even = cand & (pos_codes[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    code = pos_codes[pick]
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def test_e5m2_encode_all_bf16_vs_brute_force():
+    v = _all_finite_bf16()
+    got = fp8.encode(v, "e5m2")
+    for lo in range(0, v.size, 4096):
+        sl = slice(lo, lo + 4096)
+        assert np.array_equal(got[sl], _brute_force_e5m2(v[sl]))
+
+
+def test_e5m2_ties_saturation_sign():
+    tab = fp8.decode_table("e5m2")
+    mags = tab[:0x7C]
+    mids = (mags[:-1] + mags[1:]) / 2
+    lo_code = np.arange(0x7B)
+    expect = np.where(lo_code % 2 == 0, lo_code, lo_code + 1).astype(np.uint8)
+    assert np.array_equal(fp8.encode(mids, "e5m2"), expect)
+    assert np.array_equal(fp8.encode(-mids, "e5m2"), expect | 0x80)
+    assert fp8.encode(np.array([57344.0, 61439.0, 61440.0, 1e30, np.inf]), "e5m2").tolist() \
+        == [0x7B] * 5
+    assert fp8.encode(np.array([-0.0, 1e-30, -1e-30]), "e5m2").tolist() == [0x80, 0, 0x80]
+
+
+def test_e5m2_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(9)
+    v = np.concatenate([
+        rng.standard_normal(200000) * s for s in (1e-5, 1e-2, 1, 300, 9000)
+    ]).astype(np.float32)
+    v = v[np.abs(v) <= 57344]
+    ref = torch.from_numpy(v).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(fp8.encode(v, "e5m2"), ref)
+
+
+def test_e5m2_quantize_scale_and_error_bound():
+    assert fp8.per_tensor_scale(np.array([57344.0, 1.0]), "e5m2") == np.float32(1.0)
+    x = np.array([57344.0, 1.0, -0.25, 3.5], dtype=np.float32) * np.float32(2.0 ** -12)
+    codes, s = fp8.quantize(x, fmt="e5m2")
+    assert s == np.float32(2.0 ** -12)
+    assert np.array_equal(fp8.decode(codes, "e5m2"), [57344.0, 1.0, -0.25, 3.5])
+    # half an ulp of a 2-bit mantissa: 2^-3 relative for normals
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal(100000) * 3).astype(np.float32)
+    codes, s = fp8.quantize(v, fmt="e5m2")
+    err = np.abs(fp8.dequantize(codes, s, "e5m2") - v.astype(np.float64))
+    bound = np.maximum(np.abs(v) * 2.0 ** -3, 2.0 ** -17 * float(s)) * (1 + 1e-6)
+    assert np.all(err <= bound)

@@ -314,3 +314,70 @@ def test_fp8_row_weight_scale_scales_its_output_column():
     assert np.array_equal(q["y"][:, h], 2 * p["y"][:, h])
     others = np.arange(cfg.H) != h
     assert np.array_equal(q["y"][:, others], p["y"][:, others])
+
+
+# ------------------------------------------------------------------ E5M2
+# The other FP8 format (5 exponent, 2 mantissa bits): codes of weights, x and
+# the intermediate in E5M2, scales amax / 57344.
+
+def _e5m2_case(T=5, scales="tensor"):
+    cfg, _, tk = tiny_case("fp8", T=T)
+    w = workloads.make_weights(cfg, seed=0, device="cpu", wdtype="fp8", scales=scales,
+                               fp8_format="e5m2")
+    return cfg, w, tk
+
+
+@pytest.mark.parametrize("scales", ["tensor", "row"])
+def test_e5m2_sparse_equals_dense(scales):
+    cfg, w, tk = _e5m2_case(T=6, scales=scales)
+    kw = oracle_inputs(w, tk)
+    assert kw["fp8_format"] == "e5m2"
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, act_scales=scales, **kw)
+    yd = moe.moe_dense(K=cfg.K, act_scales=scales, **kw)
+    assert np.allclose(p["y"], yd, rtol=1e-12, atol=1e-14)
+
+
+def test_e5m2_activation_scale_and_codes():
+    cfg, w, tk = _e5m2_case()
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    amax = np.float32(np.abs(kw["x"]).max())
+    assert p["s_x"] == np.float32(amax / np.float32(57344.0))
+
+
+def test_e5m2_intermediate_error_bound():
+    """As for E4M3, with the E5M2 half-ulp: 2^-3 relative for normals and
+    2^-17 * s_a absolute in the subnormal range."""
+    cfg, w, tk = _e5m2_case(T=4)
+    kw = oracle_inputs(w, tk)
+    _, p = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    qx, s_x = fp8.quantize(kw["x"], fmt="e5m2")
+    xh = fp8.dequantize(qx, s_x, "e5m2")
+    w13f = np.stack([fp8.dequantize(kw["w13"][e], kw["w13_scale"][e], "e5m2")
+                     for e in range(cfg.E)])
+    w2f = np.stack([fp8.dequantize(kw["w2"][e], kw["w2_scale"][e], "e5m2")
+                    for e in range(cfg.E)])
+    _, pf = moe.moe_forward(xh, kw["logits"], w13f, w2f, cfg.K, return_parts=True)
+    s_a = float(p["s_a"])
+    bound = np.zeros_like(pf["y"])
+    for t in range(4):
+        for k in range(cfg.K):
+            e = p["ids"][t, k]
+            g, u = w13f[e][:cfg.I] @ xh[t], w13f[e][cfg.I:] @ xh[t]
+            a = g / (1 + np.exp(-g)) * u
+            da = np.maximum(np.abs(a) * 2.0 ** -3, 2.0 ** -17 * s_a)
+            bound[t] += p["weights"][t, k] * (np.abs(w2f[e]) @ da)
+    err = np.abs(p["y"] - pf["y"])
+    assert (err <= bound * (1 + 1e-6) + 1e-12).all()
+    assert err.max() > 0
+
+
+def test_e5m2_and_e4m3_agree_within_their_precision():
+    """The same float weights coded in either format give the same layer up
+    to the coarser format's quantisation error (a few percent of max|y|)."""
+    cfg, w4, tk = tiny_case("fp8", T=4)
+    _, w5, _ = _e5m2_case(T=4)
+    y4 = moe.moe_forward(K=cfg.K, **oracle_inputs(w4, tk))
+    y5 = moe.moe_forward(K=cfg.K, **oracle_inputs(w5, tk))
+    rel = np.abs(y5 - y4).max() / np.abs(y4).max()
+    assert 1e-3 < rel < 0.2
