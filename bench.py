@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--scales", choices=("tensor", "row"), default="tensor",
                     help="FP8 workloads: one scale per expert tensor (and per activation "
                          "tensor), or one per weight row and per activation row")
+    ap.add_argument("--fp8-format", choices=("e4m3", "e5m2"), default="e4m3",
+                    help="FP8 workloads: the code format of weights and activations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work the cpu_baseline sample aims at")
@@ -83,11 +85,12 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload, T, scales):
-    return f"{workload}/T{T}" + ("/row_scales" if scales == "row" else "")
+def traffic_key(workload, T, scales, fmt="e4m3"):
+    return (f"{workload}/T{T}" + ("/row_scales" if scales == "row" else "")
+            + ("/e5m2" if fmt == "e5m2" else ""))
 
 
-def load_traffic(workload, T, kernel, scales="tensor"):
+def load_traffic(workload, T, kernel, scales="tensor", fmt="e4m3"):
     """HBM bytes per launch of ``kernel`` from the committed counter runs, or
     None when there are none for this workload or the kernels have changed."""
     try:
@@ -95,7 +98,7 @@ def load_traffic(workload, T, kernel, scales="tensor"):
             db = json.load(fh)
     except (OSError, ValueError):
         return None
-    rec = db.get(traffic_key(workload, T, scales))
+    rec = db.get(traffic_key(workload, T, scales, fmt))
     if not rec or rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
         return None
     return rec.get("bytes_per_launch")
@@ -153,7 +156,7 @@ def record_traffic(args):
             db = json.load(fh)
     except (OSError, ValueError):
         db = {}
-    key = traffic_key(cfg.name, T, args.scales)
+    key = traffic_key(cfg.name, T, args.scales, args.fp8_format)
     db[key] = rec
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(db, fh, indent=1, sort_keys=True)
@@ -235,7 +238,7 @@ def host_weights(w):
     return Experts(w)
 
 
-def oracle_and_parity(cfg, m, w, tk, budget, scales="tensor"):
+def oracle_and_parity(cfg, m, w, tk, budget, scales="tensor", fmt="e4m3"):
     """Time the CPU oracle on sub-batches of the first n tokens (n doubling
     while the last run stays well inside ``budget`` seconds), and compare the
     library on the same sub-batch.  Returns (cpu_baseline, parity)."""
@@ -258,7 +261,8 @@ def oracle_and_parity(cfg, m, w, tk, budget, scales="tensor"):
         lh = lg.cpu().numpy()
         t0 = time.perf_counter()
         ref, parts = omoe.moe_forward(xh, lh, K=cfg.K, return_parts=True,
-                                      act_scales=scales if fp8 else "tensor", **kw)
+                                      act_scales=scales if fp8 else "tensor",
+                                      fp8_format=fmt, **kw)
         dt = time.perf_counter() - t0
         last = (n, dt, ref, parts, x, lg)
         log(f"oracle sub-batch of {n} tokens: {dt:.2f} s")
@@ -379,8 +383,9 @@ def main():
 
     wdtype = "bf16" if cfg.wdtype == "float32" else cfg.wdtype
     rows = args.scales == "row" and wdtype == "fp8"
+    fmt = args.fp8_format
     w = workloads.make_weights(cfg, seed=0, device=dev, wdtype=wdtype,
-                               scales="row" if rows else "tensor")
+                               scales="row" if rows else "tensor", fp8_format=fmt)
     tk = workloads.make_tokens(cfg, T, seed=0, device=dev)
     wbytes = w["w13"].numel() * w["w13"].element_size() + w["w2"].numel() * w["w2"].element_size()
     # Rotate weight copies when one set could stay in the 256 MB last-level
@@ -388,8 +393,8 @@ def main():
     copies = 1 if wbytes >= (1 << 30) else min(8, math.ceil((2 << 30) / wbytes))
     sets = [w] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
                   for _ in range(copies - 1)]
-    mods = [mm.FusedMoE(s["w13"], s["w2"], cfg.K, s.get("w13_scale"), s.get("w2_scale"))
-            for s in sets]
+    mods = [mm.FusedMoE(s["w13"], s["w2"], cfg.K, s.get("w13_scale"), s.get("w2_scale"),
+                        fp8_format=fmt) for s in sets]
     x, lg = tk["x"], tk["logits"]
     out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device=dev)
     _, ids, _ = mods[0](x, lg, out=out, return_topk=True)
@@ -459,7 +464,7 @@ def main():
     roof["kernel_us"] = round(dom_us, 2)
     roof["kernel_us_events_raw"] = round(dom_raw_us, 2)
     roof["event_pair_floor_us"] = round(event_floor_us, 2)
-    roof["traffic"] = load_traffic(cfg.name, T, dom, "row" if rows else "tensor")
+    roof["traffic"] = load_traffic(cfg.name, T, dom, "row" if rows else "tensor", fmt)
     roof["algorithmic_bytes"] = work.stage_bytes[dom]
     roof["algorithmic_flops"] = work.stage_flops[dom]
 
@@ -469,7 +474,7 @@ def main():
     cpu = parity = None
     if not args.no_cpu_baseline:
         cpu, parity = oracle_and_parity(cfg, mods[0], w, tk, args.cpu_budget,
-                                        "row" if rows else "tensor")
+                                        "row" if rows else "tensor", fmt)
 
     gbps = work.layer_bytes / (ms * 1e-3) / 1e9
     line = {
@@ -483,11 +488,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if cfg.wdtype == "fp8" else "bf16",
+        "dtype": f"fp8_{fmt}" if cfg.wdtype == "fp8" else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "K": cfg.K, "weights": wdtype, "routing": cfg.routing,
                    "fp8_scales": ("row" if rows else "tensor") if wdtype == "fp8" else None,
+                   "fp8_format": fmt if wdtype == "fp8" else None,
                    "active_experts": work.active, "weight_copies": copies},
         "roofline": roof,
         "cpu_baseline": cpu,

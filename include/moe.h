@@ -52,7 +52,8 @@ typedef enum {
 
 typedef enum {
   MOE_BF16 = 0,             /* expert weights are bfloat16                  */
-  MOE_FP8_E4M3 = 1          /* expert weights are OCP E4M3 codes + scales   */
+  MOE_FP8_E4M3 = 1,         /* expert weights are OCP E4M3 codes + scales   */
+  MOE_FP8_E5M2 = 2          /* expert weights are OCP E5M2 codes + scales   */
 } moe_wdtype;
 
 typedef enum {
@@ -131,8 +132,12 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes,
 /*
  * Activation quantisation with one scale per row (a0 under MOE_SCALES_ROW).
  * Each row r of cols values is quantised on its own: scales[r] = amax|x_r| /
- * 448 (1 when the row is all zero) and codes as in moe_act_quant_fp8 with
- * that scale.  Finer granularity than one scale per tensor, read from the
+ * max (1 when the row is all zero) and codes = FP8(x / scales[r]) as in
+ * moe_act_quant_fp8, where fmt selects the code format: MOE_FP8_E4M3 (max
+ * 448) or MOE_FP8_E5M2 (OCP E5M2: bias 15, max 57344; round to nearest even,
+ * saturating to +-57344; the kongchang.com page's FP8 explainer names E5M2 as
+ * the wider-range, lower-precision variant).  rows = 1 gives one scale for
+ * the whole tensor.  Finer granularity than one scale per tensor, read from the
  * kongchang.com page, "Triton Backend Routing: A Practical Path to FP8
  * Quantization" (numerical distributions differ, so a uniform scale loses
  * precision), taken down to rows.
@@ -140,10 +145,11 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes,
  *   x       [rows, cols] bfloat16 (raw 16-bit patterns), 16-byte aligned
  *   codes   [rows, cols] uint8 (out), 16-byte aligned
  *   scales  [rows] float32 (out)
- * Supported: cols % 8 == 0.  No workspace.
+ * Supported: cols % 8 == 0; fmt MOE_FP8_E4M3 or MOE_FP8_E5M2
+ * (MOE_ERR_UNSUPPORTED otherwise).  No workspace.
  */
 moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols,
-                                  uint8_t* codes, float* scales,
+                                  moe_wdtype fmt, uint8_t* codes, float* scales,
                                   hipStream_t stream);
 
 /*
@@ -165,6 +171,9 @@ moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols,
  *               W = code * w13_scale[e] (or w2_scale[e]); the intermediate
  *               a = silu(g) * u is quantised per tensor over all pairs, from
  *               its float32 value, before the down projection.
+ * MOE_FP8_E5M2: as MOE_FP8_E4M3 in either scale mode, with E5M2 codes for
+ *               the weights, x and the intermediate and 57344 in place of
+ *               448 in every activation scale (amax / 57344).
  * MOE_FP8_E4M3, fp8_scales == MOE_SCALES_ROW:
  *               x^ = per-token-row E4M3 of x (as moe_act_quant_fp8_rows);
  *               W[r, :] = code[r, :] * w13_scale[e, r] (w2_scale[e, r]); the
@@ -174,8 +183,8 @@ moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols,
  * Fields:
  *   x               [T, H] bfloat16
  *   router_logits   [T, E] float32
- *   w13             [E, 2I, H] bfloat16 or uint8 E4M3 codes
- *   w2              [E, H, I]  bfloat16 or uint8 E4M3 codes
+ *   w13             [E, 2I, H] bfloat16 or uint8 E4M3 / E5M2 codes
+ *   w2              [E, H, I]  bfloat16 or uint8 E4M3 / E5M2 codes
  *   fp8_scales      moe_fp8_scales, FP8 only (ignored for bf16)
  *   w13_scale, w2_scale  FP8 only (ignored for bf16, may be NULL):
  *                   [E] float32 with MOE_SCALES_TENSOR; [E, 2I] and [E, H]

@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(HERE, "libmoemi.so")
 
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
+MOE_FP8_E5M2 = 2
+_FP8_WDTYPE = {"e4m3": MOE_FP8_E4M3, "e5m2": MOE_FP8_E5M2}
 
 MOE_SCALES_TENSOR = 0
 MOE_SCALES_ROW = 1
@@ -73,7 +75,7 @@ _SIGS = {
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]),
     "moe_act_quant_fp8_rows": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                              ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p]),
     "moe_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FusedArgs)]),
     "moe_fused_block_m": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -184,16 +186,17 @@ def act_quant_fp8(x, stream=None):
     return codes, scale
 
 
-def act_quant_fp8_rows(x, stream=None):
+def act_quant_fp8_rows(x, fmt="e4m3", stream=None):
     """(codes uint8 [R, C], scales [R] float32) of bfloat16 x [R, C], one
-    scale per row."""
+    scale per row; fmt "e4m3" or "e5m2"."""
     if x.dim() != 2:
         raise ValueError("x must be [rows, cols]")
     xp = _dev(x, torch.bfloat16, "x")
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     scales = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
-    _check(lib().moe_act_quant_fp8_rows(xp, x.shape[0], x.shape[1], _ptr(codes), _ptr(scales),
-                                        _stream(stream)), "moe_act_quant_fp8_rows")
+    _check(lib().moe_act_quant_fp8_rows(xp, x.shape[0], x.shape[1], _FP8_WDTYPE[fmt],
+                                        _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_act_quant_fp8_rows")
     return codes, scales
 
 
@@ -209,11 +212,16 @@ class FusedMoE:
     w13 [E, 2I, H] and w2 [E, H, I] are bfloat16, or uint8 E4M3 codes with
     w13_scale / w2_scale float32: [E] (one scale per expert tensor, and per
     tensor activation scales) or [E, 2I] / [E, H] (one per weight row, and
-    per row activation scales).  The workspace is a torch buffer grown on
-    demand and reused across calls (the library allocates nothing)."""
+    per row activation scales); ``fp8_format`` says whether the codes are
+    E4M3 or E5M2.  The workspace is a torch buffer grown on demand and reused
+    across calls (the library allocates nothing)."""
 
-    def __init__(self, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True):
+    def __init__(self, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True,
+                 fp8_format="e4m3"):
         self.fp8 = w13.dtype == torch.uint8
+        if fp8_format not in _FP8_WDTYPE:
+            raise ValueError(f"fp8_format must be one of {sorted(_FP8_WDTYPE)}")
+        self.wdtype = _FP8_WDTYPE[fp8_format] if self.fp8 else MOE_BF16
         self.E, twoI, self.H = w13.shape
         self.I = twoI // 2
         self.K = K
@@ -240,7 +248,7 @@ class FusedMoE:
 
     def args(self, x, logits, out, ids=None, wts=None):
         a = FusedArgs()
-        a.wdtype = MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+        a.wdtype = self.wdtype
         a.fp8_scales = MOE_SCALES_ROW if self.rows else MOE_SCALES_TENSOR
         a.T = x.shape[0]
         a.H, a.I, a.E, a.K = self.H, self.I, self.E, self.K
@@ -258,7 +266,7 @@ class FusedMoE:
 
     def workspace_bytes(self, T):
         a = FusedArgs()
-        a.wdtype = MOE_FP8_E4M3 if self.fp8 else MOE_BF16
+        a.wdtype = self.wdtype
         a.fp8_scales = MOE_SCALES_ROW if self.rows else MOE_SCALES_TENSOR
         a.T, a.H, a.I, a.E, a.K = T, self.H, self.I, self.E, self.K
         return int(lib().moe_fused_workspace_bytes(ctypes.byref(a)))
@@ -304,7 +312,7 @@ class FusedMoE:
 
 
 def fused_forward(x, logits, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True,
-                  return_topk=False, stream=None):
+                  return_topk=False, stream=None, fp8_format="e4m3"):
     """One-shot fused forward (allocates its workspace through torch)."""
-    m = FusedMoE(w13, w2, K, w13_scale, w2_scale, renormalize)
+    m = FusedMoE(w13, w2, K, w13_scale, w2_scale, renormalize, fp8_format)
     return m(x, logits, return_topk=return_topk, stream=stream)

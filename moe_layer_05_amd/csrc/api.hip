@@ -84,8 +84,15 @@ struct FusedLayout {
   DecodeShape gu, dn;
 };
 
+bool is_fp8(moe_wdtype wd) { return wd == MOE_FP8_E4M3 || wd == MOE_FP8_E5M2; }
+bool wdtype_ok(moe_wdtype wd) { return wd == MOE_BF16 || is_fp8(wd); }
+// Operand format of the kernels for a weight type.
+int fmt_of(moe_wdtype wd) {
+  return wd == MOE_FP8_E5M2 ? kFmtE5M2 : wd == MOE_FP8_E4M3 ? kFmtE4M3 : kFmtBF16;
+}
+
 bool rows_mode(const moe_fused_args* a) {
-  return a->wdtype == MOE_FP8_E4M3 && a->fp8_scales == MOE_SCALES_ROW;
+  return is_fp8(a->wdtype) && a->fp8_scales == MOE_SCALES_ROW;
 }
 
 bool use_tiles(int64_t T, int E, int K) {
@@ -95,7 +102,7 @@ bool use_tiles(int64_t T, int E, int K) {
 FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, bool rows) {
   FusedLayout L{};
   const int64_t P = T * K;
-  const bool fp8 = wd == MOE_FP8_E4M3;
+  const bool fp8 = is_fp8(wd);
   rows = rows && fp8;
   const int welem = fp8 ? 1 : 2;
   L.tiled = use_tiles(T, E, K);
@@ -217,19 +224,21 @@ moe_status moe_act_quant_fp8(const void* x, int64_t n, uint8_t* codes, float* sc
   const int cus = num_cus();
   hipError_t e = launch_zero_amax(amax, 1, stream);
   if (e == hipSuccess && n > 0) e = launch_amax_bf16(x, n, amax, cus, stream);
-  if (e == hipSuccess) e = launch_quant_bf16(x, n, amax, codes, scale, cus, stream);
+  if (e == hipSuccess) e = launch_quant_bf16(kFmtE4M3, x, n, amax, codes, scale, cus, stream);
   return hip_status(e);
 }
 
-moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols, uint8_t* codes,
-                                  float* scales, hipStream_t stream) {
+moe_status moe_act_quant_fp8_rows(const void* x, int64_t rows, int32_t cols, moe_wdtype fmt,
+                                  uint8_t* codes, float* scales, hipStream_t stream) {
   if (rows < 0 || cols < 0) return MOE_ERR_SHAPE;
+  if (!is_fp8(fmt)) return MOE_ERR_UNSUPPORTED;
   if (cols % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (rows == 0) return MOE_OK;
   if (!x || !codes || !scales) return MOE_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
   if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_quant_rows(x, true, rows, cols, codes, scales, num_cus(), stream));
+  return hip_status(
+      launch_quant_rows(fmt_of(fmt), x, true, rows, cols, codes, scales, num_cus(), stream));
 }
 
 int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
@@ -249,8 +258,8 @@ int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,
 size_t moe_fused_workspace_bytes(const moe_fused_args* a) {
   if (!a) return 0;
   if (check_shape(a->T, a->H, a->I, a->E, a->K) != MOE_OK) return 0;
-  if (a->wdtype != MOE_BF16 && a->wdtype != MOE_FP8_E4M3) return 0;
-  if (a->wdtype == MOE_FP8_E4M3 && a->fp8_scales != MOE_SCALES_TENSOR &&
+  if (!wdtype_ok(a->wdtype)) return 0;
+  if (is_fp8(a->wdtype) && a->fp8_scales != MOE_SCALES_TENSOR &&
       a->fp8_scales != MOE_SCALES_ROW)
     return 0;
   return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype, rows_mode(a)).total;
@@ -269,8 +278,9 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   if (!a) return MOE_ERR_NULL;
   moe_status st = check_shape(a->T, a->H, a->I, a->E, a->K);
   if (st != MOE_OK) return st;
-  if (a->wdtype != MOE_BF16 && a->wdtype != MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;
-  const bool fp8 = a->wdtype == MOE_FP8_E4M3;
+  if (!wdtype_ok(a->wdtype)) return MOE_ERR_UNSUPPORTED;
+  const bool fp8 = is_fp8(a->wdtype);
+  const int fmt = fmt_of(a->wdtype);
   if (fp8 && a->fp8_scales != MOE_SCALES_TENSOR && a->fp8_scales != MOE_SCALES_ROW)
     return MOE_ERR_UNSUPPORTED;
   if (a->T == 0) return MOE_OK;
@@ -314,7 +324,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   if (!L.tiled && front_fits(T, H, K, fp8)) {
     // a1 + a0 + a2 in one launch; the act-quant and align stages are empty
     if (e == hipSuccess)
-      e = launch_front(a->router_logits, T, E, K, a->renormalize, ids, wts, fp8, a->x, H, amax_x,
+      e = launch_front(a->router_logits, T, E, K, a->renormalize, ids, wts, fmt, a->x, H, amax_x,
                        amax_a, qx, rows ? sx : nullptr, L.bm, sorted, bexp, npp, rank, stream);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
@@ -326,10 +336,11 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     // a0
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
     if (e == hipSuccess && rows) {
-      e = launch_quant_rows(a->x, true, T, H, qx, sx, cus, stream);
+      e = launch_quant_rows(fmt, a->x, true, T, H, qx, sx, cus, stream);
     } else if (fp8) {
       if (e == hipSuccess) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
-      if (e == hipSuccess) e = launch_quant_bf16(a->x, T * H, amax_x, qx, nullptr, cus, stream);
+      if (e == hipSuccess)
+        e = launch_quant_bf16(fmt, a->x, T * H, amax_x, qx, nullptr, cus, stream);
     }
     // a2
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
@@ -365,7 +376,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.act_scale = rows ? sx : nullptr;
     g.a_out = abuf;
     g.a_amax = fp8 && !rows ? amax_a : nullptr;
-    e = launch_gemm_decode(kGateUp, fp8, g, L.gu.ra, L.nblk, cus, stream);
+    e = launch_gemm_decode(kGateUp, fmt, g, L.gu.ra, L.nblk, cus, stream);
     if (e == hipSuccess && L.tiled) {
       GemmParams t = g;
       t.sorted_ids = sorted_t;
@@ -374,15 +385,16 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       t.BM = tile_block_m();
       t.groups = tile_groups(kGateUp, I);
       t.splits = 1;
-      e = launch_gemm_tile(kGateUp, fp8, t, L.nblk_t, cus, stream);
+      e = launch_gemm_tile(kGateUp, fmt, t, L.nblk_t, cus, stream);
     }
   }
   // intermediate quantisation (FP8)
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_INTER_QUANT, stream);
   if (e == hipSuccess && rows)
-    e = launch_quant_rows(abuf, false, P, I, qa, sa, cus, stream);
+    e = launch_quant_rows(fmt, abuf, false, P, I, qa, sa, cus, stream);
   else if (e == hipSuccess && fp8)
-    e = launch_quant_f32(static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus, stream);
+    e = launch_quant_f32(fmt, static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus,
+                         stream);
   // a5
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);
   if (e == hipSuccess) {
@@ -399,7 +411,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     g.dw = dw;
     g.dw_split_stride = (int64_t)P * H;
     g.dw_bf16 = L.tiled ? 1 : 0;
-    e = launch_gemm_decode(kDown, fp8, g, L.dn.ra, L.nblk, cus, stream);
+    e = launch_gemm_decode(kDown, fmt, g, L.dn.ra, L.nblk, cus, stream);
     if (e == hipSuccess && L.tiled) {
       GemmParams t = g;
       t.sorted_ids = sorted_t;
@@ -408,7 +420,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       t.BM = tile_block_m();
       t.groups = tile_groups(kDown, H);
       t.splits = 1;
-      e = launch_gemm_tile(kDown, fp8, t, L.nblk_t, cus, stream);
+      e = launch_gemm_tile(kDown, fmt, t, L.nblk_t, cus, stream);
     }
   }
   // a6

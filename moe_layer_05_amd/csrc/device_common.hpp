@@ -8,6 +8,18 @@ namespace moe {
 
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr float kFp8Max = 448.0f;   // largest finite OCP E4M3 value
+constexpr float kE5m2Max = 57344.0f;  // largest finite OCP E5M2 value
+
+// Operand formats of the expert products: bfloat16, or FP8 codes in E4M3 or
+// E5M2 (the FP8 explainer of the kongchang.com page names both).
+constexpr int kFmtBF16 = 0;
+constexpr int kFmtE4M3 = 1;
+constexpr int kFmtE5M2 = 2;
+
+template <int FMT>
+constexpr float fp8_max() {
+  return FMT == kFmtE5M2 ? kE5m2Max : kFp8Max;
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -82,16 +94,49 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
          (f32_to_e4m3(d / s) << 24);
 }
 
+// float32 -> OCP E5M2 code: nearest, ties to the even mantissa, saturating to
+// +-57344, sign kept.  As f32_to_e4m3: subnormals (< 2^-14) are scaled by
+// 2^16 and rounded to an integer mantissa (0..4; 4 is the smallest normal's
+// code), normals have their float32 mantissa rounded to 2 bits and their
+// exponent re-biased from 127 to 15.  Not for NaN.
+__device__ __forceinline__ uint32_t f32_to_e5m2(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fminf(fabsf(v), kE5m2Max);
+  uint32_t code;
+  if (a < 6.103515625e-05f) {                 // 2^-14: subnormal range
+    code = (uint32_t)__builtin_rintf(a * 65536.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0xFFFFFu + ((b >> 21) & 1u);         // RNE to 2 mantissa bits
+    code = (b >> 21) - ((127u - 15u) << 2);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ uint32_t e5m2_pack4(float a, float b, float c, float d, float s) {
+  return f32_to_e5m2(a / s) | (f32_to_e5m2(b / s) << 8) | (f32_to_e5m2(c / s) << 16) |
+         (f32_to_e5m2(d / s) << 24);
+}
+
+// Four codes of format FMT (E4M3 or E5M2) of v / s in one word.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d, float s) {
+  if constexpr (FMT == kFmtE5M2) return e5m2_pack4(a, b, c, d, s);
+  else return e4m3_pack4(a, b, c, d, s);
+}
+
 // silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) and
 // exponential; for very negative z, e^-z is +inf and the result is -0.
 __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
-// Activation scale from an amax stored as float bits: amax / 448, 1 if zero.
-__device__ __forceinline__ float scale_from_amax_bits(uint32_t amax_bits) {
+// Activation scale from an amax stored as float bits: amax / max of the
+// format (448 for E4M3), 1 if zero.
+__device__ __forceinline__ float scale_from_amax_bits(uint32_t amax_bits,
+                                                      float fmax = kFp8Max) {
   float amax = __uint_as_float(amax_bits);
-  return amax > 0.0f ? amax / kFp8Max : 1.0f;
+  return amax > 0.0f ? amax / fmax : 1.0f;
 }
 
 // ---------------------------------------------------------------- waves

@@ -10,7 +10,8 @@
 //    tokens), then after a workgroup barrier the whole workgroup runs the
 //    align step on the ids just written (align_block).
 //  - (FP8) Workgroups 1..n: each reduces the amax of all of x and writes the
-//    codes E4M3(x / s), s = amax / 448, of its own slice (the same arithmetic
+//    codes FP8(x / s), s = amax / max (448 for E4M3, 57344 for E5M2), of its
+//    own slice (the same arithmetic
 //    as the two-kernel path, so the codes are identical); workgroup 1 stores
 //    the final amax word for the GEMM epilogue and clears the slots of the
 //    intermediate's amax.  With per-row scales workgroup 1 + t quantises
@@ -48,8 +49,9 @@ struct FrontArgs {
 // amax of all of x (a few hundred KB at most, from L2) and writes the codes
 // of its own slice, so the divisions are spread over many compute units and
 // need no exchange between workgroups.
-template <int VPL, bool FP8>
+template <int VPL, int FMT>
 __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
+  constexpr bool FP8 = FMT != kFmtBF16;
   extern __shared__ int smem[];
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -73,13 +75,13 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
       if (lane == 0) wmax[wave] = m;
       __syncthreads();
       m = wave_max_dpp(wmax[lane & (kAlignWaves - 1)]);
-      const float s = scale_from_amax_bits(__float_as_uint(m));
+      const float s = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
       if (tid == 0) a.sx_rows[blockIdx.x - 1] = s;
       for (int64_t j = tid; j < h8; j += kAlignThreads) {
         const uint4 q = a.x[base + j];
         uint2 o;
-        o.x = e4m3_pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
-        o.y = e4m3_pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
+        o.x = fp8_pack4<FMT>(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
+        o.y = fp8_pack4<FMT>(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
         a.qx[base + j] = o;
       }
       return;
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
       if (lane == 0) wmax[wave] = m;
       __syncthreads();
       m = wave_max_dpp(wmax[lane & (kAlignWaves - 1)]);
-      const float s = scale_from_amax_bits(__float_as_uint(m));
+      const float s = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
       if (blockIdx.x == 1) {
         if (tid == 0) a.amax_x[kAmaxFinal] = __float_as_uint(m);
         if (tid < kAmaxSlots) a.amax_a[amax_zero_index(tid)] = 0u;
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
       for (int64_t j = j0 + tid; j < j1; j += kAlignThreads) {
         const uint4 q = a.x[j];
         uint2 o;
-        o.x = e4m3_pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
-        o.y = e4m3_pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
+        o.x = fp8_pack4<FMT>(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
+        o.y = fp8_pack4<FMT>(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
         a.qx[j] = o;
       }
       return;
@@ -134,36 +136,34 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
   align_block(a.ids, a.T * a.K, a.E, a.out, a.rank, smem);
 }
 
-template <bool FP8>
+template <int FMT>
 hipError_t launch_vpl(const FrontArgs& a, int vpl, size_t lds, hipStream_t stream) {
+  constexpr bool FP8 = FMT != kFmtBF16;
   // FP8: one workgroup per kXSlice 16-byte pieces of x, or per token row
   // with per-row scales, after workgroup 0
   const unsigned nq = !FP8 ? 0u
                       : a.sx_rows ? (unsigned)a.T
                                   : (unsigned)((a.n8 + kXSlice - 1) / kXSlice);
   const dim3 grid(1 + (nq > 0 ? nq : (FP8 ? 1u : 0u))), block(kAlignThreads);
-  if (vpl <= 1) front_kernel<1, FP8><<<grid, block, lds, stream>>>(a);
-  else if (vpl <= 2) front_kernel<2, FP8><<<grid, block, lds, stream>>>(a);
-  else if (vpl <= 4) front_kernel<4, FP8><<<grid, block, lds, stream>>>(a);
-  else if (vpl <= 8) front_kernel<8, FP8><<<grid, block, lds, stream>>>(a);
-  else front_kernel<16, FP8><<<grid, block, lds, stream>>>(a);
+  if (vpl <= 1) front_kernel<1, FMT><<<grid, block, lds, stream>>>(a);
+  else if (vpl <= 2) front_kernel<2, FMT><<<grid, block, lds, stream>>>(a);
+  else if (vpl <= 4) front_kernel<4, FMT><<<grid, block, lds, stream>>>(a);
+  else if (vpl <= 8) front_kernel<8, FMT><<<grid, block, lds, stream>>>(a);
+  else front_kernel<16, FMT><<<grid, block, lds, stream>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t prepare_front_kernels() {
-  const void* fns[] = {
-      reinterpret_cast<const void*>(&front_kernel<1, false>),
-      reinterpret_cast<const void*>(&front_kernel<2, false>),
-      reinterpret_cast<const void*>(&front_kernel<4, false>),
-      reinterpret_cast<const void*>(&front_kernel<8, false>),
-      reinterpret_cast<const void*>(&front_kernel<16, false>),
-      reinterpret_cast<const void*>(&front_kernel<1, true>),
-      reinterpret_cast<const void*>(&front_kernel<2, true>),
-      reinterpret_cast<const void*>(&front_kernel<4, true>),
-      reinterpret_cast<const void*>(&front_kernel<8, true>),
-      reinterpret_cast<const void*>(&front_kernel<16, true>)};
+#define MOE_FRONT_FNS(F)                                      \
+  reinterpret_cast<const void*>(&front_kernel<1, F>),         \
+      reinterpret_cast<const void*>(&front_kernel<2, F>),     \
+      reinterpret_cast<const void*>(&front_kernel<4, F>),     \
+      reinterpret_cast<const void*>(&front_kernel<8, F>),     \
+      reinterpret_cast<const void*>(&front_kernel<16, F>)
+  const void* fns[] = {MOE_FRONT_FNS(kFmtBF16), MOE_FRONT_FNS(kFmtE4M3), MOE_FRONT_FNS(kFmtE5M2)};
+#undef MOE_FRONT_FNS
   for (const void* f : fns) {
     const hipError_t e = prepare_kernel(f, 0);
     if (e != hipSuccess) return e;
@@ -179,7 +179,7 @@ bool front_fits(int64_t T, int H, int K, bool fp8) {
 }
 
 hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm, int32_t* ids,
-                        float* wts, bool fp8, const void* x, int H, uint32_t* amax_x,
+                        float* wts, int fmt, const void* x, int H, uint32_t* amax_x,
                         uint32_t* amax_a, uint8_t* qx, float* sx_rows, int BM,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
                         int32_t* rank, hipStream_t stream) {
@@ -202,7 +202,9 @@ hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm
   const int vpl = (E + kWave - 1) / kWave;
   size_t lds = align_lds_words(E) * sizeof(int);
   if (lds < kAlignWaves * sizeof(float)) lds = kAlignWaves * sizeof(float);
-  return fp8 ? launch_vpl<true>(a, vpl, lds, stream) : launch_vpl<false>(a, vpl, lds, stream);
+  if (fmt == kFmtE4M3) return launch_vpl<kFmtE4M3>(a, vpl, lds, stream);
+  if (fmt == kFmtE5M2) return launch_vpl<kFmtE5M2>(a, vpl, lds, stream);
+  return launch_vpl<kFmtBF16>(a, vpl, lds, stream);
 }
 
 }  // namespace moe

@@ -40,6 +40,7 @@
 //    in a fixed order, so results stay deterministic.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -108,11 +109,12 @@ constexpr int ring_depth(int ra, int nsub) {
                              : (nsub == 2 ? (ra == 4 ? 3 : (ra == 2 ? 3 : 4)) : 2);
 }
 
-template <bool FP8>
+template <int FMT>
 struct Tile {
   // 16x16 accumulate of one 256-byte chunk: A = 16 weight rows, B = 16 tokens.
   static __device__ __forceinline__ v4f mma(const uint4 (&a)[4], const uint4 (&b)[4], v4f acc) {
-    if constexpr (FP8) {
+    if constexpr (FMT != kFmtBF16) {
+      constexpr int kF = FMT == kFmtE5M2 ? 1 : 0;  // operand format: 0 E4M3, 1 E5M2
       v8i a0 = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
                 (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
       v8i b0 = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
@@ -121,9 +123,9 @@ struct Tile {
                 (int)a[3].x, (int)a[3].y, (int)a[3].z, (int)a[3].w};
       v8i b1 = {(int)b[2].x, (int)b[2].y, (int)b[2].z, (int)b[2].w,
                 (int)b[3].x, (int)b[3].y, (int)b[3].z, (int)b[3].w};
-      // format 0 = E4M3 for both operands; scales 2^(127-127) = 1
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, 0, 0, 0, 127, 0, 127);
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, 0, 0, 0, 127, 0, 127);
+      // the same format for both operands; scales 2^(127-127) = 1
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a0, b0, acc, kF, kF, 0, 127, 0, 127);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a1, b1, acc, kF, kF, 0, 127, 0, 127);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -136,8 +138,9 @@ struct Tile {
   }
 };
 
-template <int MODE, bool FP8, int NSUB, int RA, int D>
+template <int MODE, int FMT, int NSUB, int RA, int D>
 __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
+  constexpr bool FP8 = FMT != kFmtBF16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // loads per chunk, all into LDS: 4 per 16-row weight tile, 4 per 16-token tile
   constexpr int kTiles = RA + NSUB;
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
       const uint32_t o = (uint32_t)(d * kTiles + ra) * kTileBytes;
       lds_read4(a, rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[ra][s] = Tile<FP8>::mma(a, bt[s], acc[ra][s]);
+      for (int s = 0; s < NSUB; ++s) acc[ra][s] = Tile<FMT>::mma(a, bt[s], acc[ra][s]);
     }
   };
 
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
   const bool rows = FP8 && p.row_scales;
   const int64_t wrow0 = (int64_t)e * (MODE == kGateUp ? 2 * p.I : p.H);
   if constexpr (FP8)
-    if (!rows) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[e];
+    if (!rows) scale = scale_from_amax_bits(*p.act_amax, fp8_max<FMT>()) * p.w_scale[e];
 
   if constexpr (MODE == kGateUp) {
     float local_max = 0.0f;
@@ -441,8 +444,9 @@ __device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
   return v;
 }
 
-template <int MODE, bool FP8, int NSUB, int RA, int D>
+template <int MODE, int FMT, int NSUB, int RA, int D>
 __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
+  constexpr bool FP8 = FMT != kFmtBF16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int kTiles = RA + NSUB;
   constexpr int kLoads = 4 * kTiles;
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
   const int64_t u0 = blockIdx.x, du = gridDim.x;
   if (u0 >= total) return;
   float act_scale = 1.0f;
-  if constexpr (FP8) act_scale = scale_from_amax_bits(*p.act_amax);
+  if constexpr (FP8) act_scale = scale_from_amax_bits(*p.act_amax, fp8_max<FMT>());
 
   const int nw = (int)((total - 1 - u0) / du) + 1;         // units of this wave
   const int row_bytes = (int)p.row_bytes;
@@ -595,7 +599,7 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
       const uint32_t o = (uint32_t)(d * kTiles + ra) * kTileBytes;
       lds_read4(a, rd[0] + o, rd[1] + o, rd[2] + o, rd[3] + o);
 #pragma unroll
-      for (int s = 0; s < NSUB; ++s) acc[ra][s] = Tile<FP8>::mma(a, bt[s], acc[ra][s]);
+      for (int s = 0; s < NSUB; ++s) acc[ra][s] = Tile<FMT>::mma(a, bt[s], acc[ra][s]);
     }
   };
   auto epilogue = [&](int k) {
@@ -686,10 +690,10 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
 
 // Kernel preparation (dynamic LDS limits), run once per device by the entry
 // points before any launch (prepare_decode_kernels).
-template <int MODE, bool FP8, int NSUB, int RA, int D>
+template <int MODE, int FMT, int NSUB, int RA, int D>
 hipError_t ready_one() {
   return prepare_kernel(
-      reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D>),
+      reinterpret_cast<const void*>(&moe_gemm_decode_kernel<MODE, FMT, NSUB, RA, D>),
       D * (RA + NSUB) * kTileBytes);
 }
 
@@ -698,17 +702,17 @@ constexpr int stream_lds(int d, int tiles, int cps) {
   return d * tiles * kTileBytes + meta_slots(d, cps) * kMetaBytes;
 }
 
-template <int MODE, bool FP8, int NSUB, int RA, int D>
+template <int MODE, int FMT, int NSUB, int RA, int D>
 hipError_t ready_stream() {                        // the limit for the most slots (cps = 1)
   return prepare_kernel(
-      reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, D>),
+      reinterpret_cast<const void*>(&moe_gemm_stream_kernel<MODE, FMT, NSUB, RA, D>),
       stream_lds(D, RA + NSUB, 1));
 }
 
-template <int MODE, bool FP8, int NSUB, int RA, int D>
+template <int MODE, int FMT, int NSUB, int RA, int D>
 hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
   const int lds = D * (RA + NSUB) * kTileBytes;
-  moe_gemm_decode_kernel<MODE, FP8, NSUB, RA, D><<<grid, dim3(64), lds, stream>>>(p);
+  moe_gemm_decode_kernel<MODE, FMT, NSUB, RA, D><<<grid, dim3(64), lds, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -717,7 +721,7 @@ hipError_t launch_one(const GemmParams& p, dim3 grid, hipStream_t stream) {
 // with many units, and for one-chunk rows, the one-wave-per-unit grid with
 // ring depth DC measured faster); the parts of the reduction must be equal.
 // Grid = the waves resident on `num_cus` compute units.
-template <int MODE, bool FP8, int NSUB, int RA, int DC, int DS>
+template <int MODE, int FMT, int NSUB, int RA, int DC, int DS>
 hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t stream) {
   const int64_t nchunks = (p.row_bytes + kChunk - 1) / kChunk;
   const int cps = (int)(nchunks / p.splits);
@@ -727,13 +731,13 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
   // slots, so per-row scales take the classic form.
   const bool stream_ok = !p.row_scales && DS > 1 && nchunks % p.splits == 0 && cps >= 1 &&
                          grid.x >= 2 * resident && grid.x < 8 * resident;
-  if (!stream_ok) return launch_one<MODE, FP8, NSUB, RA, DC>(p, grid, stream);
+  if (!stream_ok) return launch_one<MODE, FMT, NSUB, RA, DC>(p, grid, stream);
   const unsigned g = (unsigned)std::min<int64_t>(grid.x, resident);
-  moe_gemm_stream_kernel<MODE, FP8, NSUB, RA, DS><<<dim3(g), dim3(64), lds, stream>>>(p);
+  moe_gemm_stream_kernel<MODE, FMT, NSUB, RA, DS><<<dim3(g), dim3(64), lds, stream>>>(p);
   return hipGetLastError();
 }
 
-template <int MODE, bool FP8, int RA>
+template <int MODE, int FMT, int RA>
 hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
                        hipStream_t stream) {
   if constexpr (RA >= 8) {
@@ -743,23 +747,23 @@ hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus
     // one chunk per row: the one-wave-per-unit form needs no ring, so the LDS
     // holds more waves; the stream form keeps its ring across units
     switch (nsub_max) {
-      case 1: return launch_best<MODE, FP8, 1, RA, 1, ring_depth(RA, 1)>(p, grid, num_cus, stream);
-      case 2: return launch_best<MODE, FP8, 2, RA, 1, ring_depth(RA, 2)>(p, grid, num_cus, stream);
+      case 1: return launch_best<MODE, FMT, 1, RA, 1, ring_depth(RA, 1)>(p, grid, num_cus, stream);
+      case 2: return launch_best<MODE, FMT, 2, RA, 1, ring_depth(RA, 2)>(p, grid, num_cus, stream);
       case 4:
         if constexpr (RA < 8)
-          return launch_best<MODE, FP8, 4, RA, 1, ring_depth(RA, 4)>(p, grid, num_cus, stream);
+          return launch_best<MODE, FMT, 4, RA, 1, ring_depth(RA, 4)>(p, grid, num_cus, stream);
         return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
   switch (nsub_max) {
-    case 1: return launch_best<MODE, FP8, 1, RA, ring_depth(RA, 1), ring_depth(RA, 1)>(
+    case 1: return launch_best<MODE, FMT, 1, RA, ring_depth(RA, 1), ring_depth(RA, 1)>(
         p, grid, num_cus, stream);
-    case 2: return launch_best<MODE, FP8, 2, RA, ring_depth(RA, 2), ring_depth(RA, 2)>(
+    case 2: return launch_best<MODE, FMT, 2, RA, ring_depth(RA, 2), ring_depth(RA, 2)>(
         p, grid, num_cus, stream);
     case 4:
       if constexpr (RA < 8)
-        return launch_best<MODE, FP8, 4, RA, ring_depth(RA, 4), ring_depth(RA, 4)>(
+        return launch_best<MODE, FMT, 4, RA, ring_depth(RA, 4), ring_depth(RA, 4)>(
             p, grid, num_cus, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
@@ -767,42 +771,45 @@ hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus
 }
 
 template <int MODE, int RA>
-hipError_t launch_dtype(bool fp8, const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
+hipError_t launch_dtype(int fmt, const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
                         hipStream_t stream) {
-  return fp8 ? launch_nsub<MODE, true, RA>(p, nsub_max, grid, num_cus, stream)
-             : launch_nsub<MODE, false, RA>(p, nsub_max, grid, num_cus, stream);
+  if (fmt == kFmtE4M3) return launch_nsub<MODE, kFmtE4M3, RA>(p, nsub_max, grid, num_cus, stream);
+  if (fmt == kFmtE5M2) return launch_nsub<MODE, kFmtE5M2, RA>(p, nsub_max, grid, num_cus, stream);
+  return launch_nsub<MODE, kFmtBF16, RA>(p, nsub_max, grid, num_cus, stream);
 }
 
-template <int MODE, bool FP8, int RA, int NSUB>
+template <int MODE, int FMT, int RA, int NSUB>
 hipError_t ready_shape() {
-  hipError_t e = ready_one<MODE, FP8, NSUB, RA, 1>();
-  if (e == hipSuccess) e = ready_one<MODE, FP8, NSUB, RA, ring_depth(RA, NSUB)>();
-  if (e == hipSuccess) e = ready_stream<MODE, FP8, NSUB, RA, ring_depth(RA, NSUB)>();
+  hipError_t e = ready_one<MODE, FMT, NSUB, RA, 1>();
+  if (e == hipSuccess) e = ready_one<MODE, FMT, NSUB, RA, ring_depth(RA, NSUB)>();
+  if (e == hipSuccess) e = ready_stream<MODE, FMT, NSUB, RA, ring_depth(RA, NSUB)>();
   return e;
 }
 
-template <int MODE, bool FP8, int RA>
+template <int MODE, int FMT, int RA>
 hipError_t ready_ra() {
-  hipError_t e = ready_shape<MODE, FP8, RA, 1>();
-  if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 2>();
+  hipError_t e = ready_shape<MODE, FMT, RA, 1>();
+  if (e == hipSuccess) e = ready_shape<MODE, FMT, RA, 2>();
   if constexpr (RA < 8)                            // RA = 8 takes at most 2 token tiles
-    if (e == hipSuccess) e = ready_shape<MODE, FP8, RA, 4>();
+    if (e == hipSuccess) e = ready_shape<MODE, FMT, RA, 4>();
   return e;
 }
 
 }  // namespace
 
 hipError_t prepare_decode_kernels() {
-  hipError_t e = ready_ra<kGateUp, false, 2>();
-  if (e == hipSuccess) e = ready_ra<kGateUp, false, 4>();
-  if (e == hipSuccess) e = ready_ra<kGateUp, true, 2>();
-  if (e == hipSuccess) e = ready_ra<kGateUp, true, 4>();
-  if (e == hipSuccess) e = ready_ra<kDown, false, 2>();
-  if (e == hipSuccess) e = ready_ra<kDown, false, 4>();
-  if (e == hipSuccess) e = ready_ra<kDown, true, 2>();
-  if (e == hipSuccess) e = ready_ra<kDown, true, 4>();
-  if (e == hipSuccess) e = ready_ra<kDown, false, 8>();
-  if (e == hipSuccess) e = ready_ra<kDown, true, 8>();
+  hipError_t e = hipSuccess;
+  auto all = [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    if (e == hipSuccess) e = ready_ra<kGateUp, F, 2>();
+    if (e == hipSuccess) e = ready_ra<kGateUp, F, 4>();
+    if (e == hipSuccess) e = ready_ra<kDown, F, 2>();
+    if (e == hipSuccess) e = ready_ra<kDown, F, 4>();
+    if (e == hipSuccess) e = ready_ra<kDown, F, 8>();
+  };
+  all(std::integral_constant<int, kFmtBF16>{});
+  all(std::integral_constant<int, kFmtE4M3>{});
+  all(std::integral_constant<int, kFmtE5M2>{});
   return e;
 }
 
@@ -872,7 +879,7 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
   return s;
 }
 
-hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
+hipError_t launch_gemm_decode(int mode, int fmt, const GemmParams& p, int ra, int64_t nblk_cap,
                               int num_cus, hipStream_t stream) {
   const int nsub_max = p.BM / 16;
   const int64_t wgs = nblk_cap * p.groups * p.splits;   // one wave each
@@ -880,13 +887,13 @@ hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, i
   if (wgs > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;
   dim3 grid((unsigned)wgs);
   if (mode == kGateUp) {
-    if (ra == 2) return launch_dtype<kGateUp, 2>(fp8, p, nsub_max, grid, num_cus, stream);
-    if (ra == 4) return launch_dtype<kGateUp, 4>(fp8, p, nsub_max, grid, num_cus, stream);
+    if (ra == 2) return launch_dtype<kGateUp, 2>(fmt, p, nsub_max, grid, num_cus, stream);
+    if (ra == 4) return launch_dtype<kGateUp, 4>(fmt, p, nsub_max, grid, num_cus, stream);
     return hipErrorInvalidValue;
   }
-  if (ra == 2) return launch_dtype<kDown, 2>(fp8, p, nsub_max, grid, num_cus, stream);
-  if (ra == 4) return launch_dtype<kDown, 4>(fp8, p, nsub_max, grid, num_cus, stream);
-  if (ra == 8) return launch_dtype<kDown, 8>(fp8, p, nsub_max, grid, num_cus, stream);
+  if (ra == 2) return launch_dtype<kDown, 2>(fmt, p, nsub_max, grid, num_cus, stream);
+  if (ra == 4) return launch_dtype<kDown, 4>(fmt, p, nsub_max, grid, num_cus, stream);
+  if (ra == 8) return launch_dtype<kDown, 8>(fmt, p, nsub_max, grid, num_cus, stream);
   return hipErrorInvalidValue;
 }
 

@@ -62,14 +62,15 @@ __device__ __forceinline__ void lds_read4(uint4 (&d)[4], uint32_t a0, uint32_t a
       : "memory");
 }
 
-template <bool FP8>
+template <int FMT>
 __device__ __forceinline__ v4f tile_mma(const uint4 (&a)[2], const uint4 (&b)[2], v4f acc) {
-  if constexpr (FP8) {
+  if constexpr (FMT != kFmtBF16) {
+    constexpr int kF = FMT == kFmtE5M2 ? 1 : 0;    // operand format: 0 E4M3, 1 E5M2
     v8i av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
               (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
     v8i bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
               (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, kF, kF, 0, 127, 0, 127);
   } else {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[0]),
                                                   __builtin_bit_cast(v8bf, b[0]), acc, 0, 0, 0);
@@ -99,8 +100,9 @@ __device__ __forceinline__ void lds_read8(uint4 (&d)[8], const uint32_t (&a)[8])
 constexpr int kWaves = 8;
 constexpr int kLoadsPerWave = 32 / kWaves;       // 1 KB loads per tile (A or B) per wave
 
-template <int MODE, bool FP8>
+template <int MODE, int FMT>
 __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
+  constexpr bool FP8 = FMT != kFmtBF16;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -242,8 +244,8 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
         const uint4 bb[2] = {bt[2 * bj], bt[2 * bj + 1]};
         const uint4 a0[2] = {cur[0], cur[1]};
         const uint4 a1[2] = {cur[2], cur[3]};
-        acc[ai][bj] = tile_mma<FP8>(a0, bb, acc[ai][bj]);
-        acc[ai + 1][bj] = tile_mma<FP8>(a1, bb, acc[ai + 1][bj]);
+        acc[ai][bj] = tile_mma<FMT>(a0, bb, acc[ai][bj]);
+        acc[ai + 1][bj] = tile_mma<FMT>(a1, bb, acc[ai + 1][bj]);
       }
     }
   };
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     float scale = 1.0f;
     const int64_t wrow0 = (int64_t)s.e * (MODE == kGateUp ? 2 * p.I : p.H);
     if constexpr (FP8)
-      if (!rows) scale = scale_from_amax_bits(*p.act_amax) * p.w_scale[s.e];
+      if (!rows) scale = scale_from_amax_bits(*p.act_amax, fp8_max<FMT>()) * p.w_scale[s.e];
     if constexpr (MODE == kGateUp) {
       float local_max = 0.0f;
 #pragma unroll
@@ -350,24 +352,26 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
 
 // Run once per device by the entry points before any launch
 // (prepare_tile_kernels): the 128 KB LDS limit.
-template <int MODE, bool FP8>
+template <int MODE, int FMT>
 hipError_t ready_tile() {
-  return prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FP8>), kTileLds);
+  return prepare_kernel(reinterpret_cast<const void*>(&moe_gemm_tile_kernel<MODE, FMT>), kTileLds);
 }
 
-template <int MODE, bool FP8>
+template <int MODE, int FMT>
 hipError_t launch_tile(const GemmParams& p, dim3 grid, hipStream_t stream) {
-  moe_gemm_tile_kernel<MODE, FP8><<<grid, dim3(64 * kWaves), kTileLds, stream>>>(p);
+  moe_gemm_tile_kernel<MODE, FMT><<<grid, dim3(64 * kWaves), kTileLds, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t prepare_tile_kernels() {
-  hipError_t e = ready_tile<kGateUp, false>();
-  if (e == hipSuccess) e = ready_tile<kGateUp, true>();
-  if (e == hipSuccess) e = ready_tile<kDown, false>();
-  if (e == hipSuccess) e = ready_tile<kDown, true>();
+  hipError_t e = ready_tile<kGateUp, kFmtBF16>();
+  if (e == hipSuccess) e = ready_tile<kGateUp, kFmtE4M3>();
+  if (e == hipSuccess) e = ready_tile<kGateUp, kFmtE5M2>();
+  if (e == hipSuccess) e = ready_tile<kDown, kFmtBF16>();
+  if (e == hipSuccess) e = ready_tile<kDown, kFmtE4M3>();
+  if (e == hipSuccess) e = ready_tile<kDown, kFmtE5M2>();
   return e;
 }
 
@@ -377,7 +381,7 @@ int tile_groups(int mode, int rows) {
   return mode == kGateUp ? (rows + 127) / 128 : (rows + kTM - 1) / kTM;
 }
 
-hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
+hipError_t launch_gemm_tile(int mode, int fmt, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream) {
   if (p.BM != kTN) return hipErrorInvalidValue;
   const int64_t tiles = nblk_cap * p.groups;
@@ -386,11 +390,14 @@ hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nbl
   // one workgroup per compute unit (a multiple of 8: one share per XCD)
   int64_t wgs = std::min<int64_t>(std::max(num_cus / 8, 1), (tiles + 7) / 8) * 8;
   dim3 grid((unsigned)wgs);
-  if (mode == kGateUp)
-    return fp8 ? launch_tile<kGateUp, true>(p, grid, stream)
-               : launch_tile<kGateUp, false>(p, grid, stream);
-  return fp8 ? launch_tile<kDown, true>(p, grid, stream)
-             : launch_tile<kDown, false>(p, grid, stream);
+  if (mode == kGateUp) {
+    if (fmt == kFmtE4M3) return launch_tile<kGateUp, kFmtE4M3>(p, grid, stream);
+    if (fmt == kFmtE5M2) return launch_tile<kGateUp, kFmtE5M2>(p, grid, stream);
+    return launch_tile<kGateUp, kFmtBF16>(p, grid, stream);
+  }
+  if (fmt == kFmtE4M3) return launch_tile<kDown, kFmtE4M3>(p, grid, stream);
+  if (fmt == kFmtE5M2) return launch_tile<kDown, kFmtE5M2>(p, grid, stream);
+  return launch_tile<kDown, kFmtBF16>(p, grid, stream);
 }
 
 }  // namespace moe

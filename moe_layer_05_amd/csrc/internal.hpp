@@ -63,7 +63,7 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
 // row, written to sx_rows -- and the align layout with block size BM.
 bool front_fits(int64_t T, int H, int K, bool fp8);
 hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm, int32_t* ids,
-                        float* wts, bool fp8, const void* x, int H, uint32_t* amax_x,
+                        float* wts, int fmt, const void* x, int H, uint32_t* amax_x,
                         uint32_t* amax_a, uint8_t* qx, float* sx_rows, int BM,
                         int32_t* sorted_ids, int32_t* block_expert, int32_t* num_post_pad,
                         int32_t* rank, hipStream_t stream);
@@ -81,13 +81,14 @@ hipError_t launch_align_split_multi(const int32_t* ids, int P, int E, int BM_sma
 hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream);
 hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
                             hipStream_t stream);
-hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
+// fmt: kFmtE4M3 or kFmtE5M2 (device_common.hpp).
+hipError_t launch_quant_bf16(int fmt, const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
                              float* scale_out, int num_cus, hipStream_t stream);
-// Per-row E4M3: scales[r] = amax|row r| / 448 (1 when 0), codes = E4M3(v /
+// Per-row FP8: scales[r] = amax|row r| / max (1 when 0), codes = FP8(v /
 // scales[r]); rows of C values (C % 8 == 0), bfloat16 or float32.
-hipError_t launch_quant_rows(const void* src, bool bf16, int64_t rows, int C, uint8_t* codes,
-                             float* scales, int num_cus, hipStream_t stream);
-hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_rows(int fmt, const void* src, bool bf16, int64_t rows, int C,
+                             uint8_t* codes, float* scales, int num_cus, hipStream_t stream);
+hipError_t launch_quant_f32(int fmt, const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream);
 
 // Resolve a kernel in the runtime ahead of its first launch (with the dynamic
@@ -110,14 +111,14 @@ hipError_t prepare_quant_kernels();
 hipError_t prepare_combine_kernels();
 
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm);
-hipError_t launch_gemm_decode(int mode, bool fp8, const GemmParams& p, int ra, int64_t nblk_cap,
+hipError_t launch_gemm_decode(int mode, int fmt, const GemmParams& p, int ra, int64_t nblk_cap,
                               int num_cus, hipStream_t stream);
 
 // Tiled products for large token blocks (BM = tile_block_m()); groups are
 // the column tiles per block.
 int tile_block_m();
 int tile_groups(int mode, int rows);
-hipError_t launch_gemm_tile(int mode, bool fp8, const GemmParams& p, int64_t nblk_cap,
+hipError_t launch_gemm_tile(int mode, int fmt, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream);
 
 // out[t] = bf16(sum over k, then parts, of w[t*K+k] * dw[part][t*K+k]); dw

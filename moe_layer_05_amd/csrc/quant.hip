@@ -1,4 +1,5 @@
-// a0 and the intermediate quantisation of a4: E4M3 per tensor, or per row.
+// a0 and the intermediate quantisation of a4: FP8 (E4M3 or E5M2) per tensor,
+// or per row.
 //
 // FP8 E4M3 (4 exponent, 3 mantissa bits) with one scale per tensor:
 // kongchang.com page, FP8 explainer under "Triton Backend Routing"; aib.vote
@@ -39,13 +40,14 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint4* __restrict_
     amax_slot_max(amax, blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave, m);
 }
 
-// codes = E4M3(x / s), 8 bfloat16 in -> 8 codes out per thread per step.
+// codes = FP8(x / s), 8 bfloat16 in -> 8 codes out per thread per step.
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint4* __restrict__ x, int64_t n8,
                                                          uint32_t* __restrict__ amax,
                                                          uint2* __restrict__ codes,
                                                          float* __restrict__ scale_out) {
   const float m = amax_slots_reduce(amax);
-  const float s = scale_from_amax_bits(__float_as_uint(m));
+  const float s = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     amax[kAmaxFinal] = __float_as_uint(m);
     if (scale_out) *scale_out = s;
@@ -54,26 +56,27 @@ __global__ __launch_bounds__(256) void quant_bf16_kernel(const uint4* __restrict
        j += (int64_t)gridDim.x * blockDim.x) {
     uint4 q = x[j];
     uint2 o;
-    o.x = e4m3_pack4(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
-    o.y = e4m3_pack4(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
+    o.x = fp8_pack4<FMT>(bf16_lo(q.x), bf16_hi(q.x), bf16_lo(q.y), bf16_hi(q.y), s);
+    o.y = fp8_pack4<FMT>(bf16_lo(q.z), bf16_hi(q.z), bf16_lo(q.w), bf16_hi(q.w), s);
     codes[j] = o;
   }
 }
 
-// codes = E4M3(a / s) for float32 a (n % 8 == 0), the amax came from the
+// codes = FP8(a / s) for float32 a (n % 8 == 0), the amax came from the
 // producer of a.
+template <int FMT>
 __global__ __launch_bounds__(256) void quant_f32_kernel(const float4* __restrict__ a, int64_t n8,
                                                         uint32_t* __restrict__ amax,
                                                         uint2* __restrict__ codes) {
   const float m = amax_slots_reduce(amax);
-  const float s = scale_from_amax_bits(__float_as_uint(m));
+  const float s = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
   if (blockIdx.x == 0 && threadIdx.x == 0) amax[kAmaxFinal] = __float_as_uint(m);
   for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n8;
        j += (int64_t)gridDim.x * blockDim.x) {
     float4 p = a[2 * j], q = a[2 * j + 1];
     uint2 o;
-    o.x = e4m3_pack4(p.x, p.y, p.z, p.w, s);
-    o.y = e4m3_pack4(q.x, q.y, q.z, q.w, s);
+    o.x = fp8_pack4<FMT>(p.x, p.y, p.z, p.w, s);
+    o.y = fp8_pack4<FMT>(q.x, q.y, q.z, q.w, s);
     codes[j] = o;
   }
 }
@@ -96,7 +99,7 @@ __device__ __forceinline__ void load8(const void* src, int64_t j, float (&v)[8])
   }
 }
 
-template <bool BF16>
+template <bool BF16, int FMT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ src,
                                                          int64_t rows, int c8,
                                                          uint2* __restrict__ codes,
@@ -115,15 +118,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
     }
     m = wave_max_dpp(m);
-    const float s = scale_from_amax_bits(__float_as_uint(m));
+    const float s = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
     if (lane == 0) scales[r] = s;
 #pragma unroll 4
     for (int j = lane; j < c8; j += kWave) {
       float v[8];
       load8<BF16>(src, base + j, v);
       uint2 o;
-      o.x = e4m3_pack4(v[0], v[1], v[2], v[3], s);
-      o.y = e4m3_pack4(v[4], v[5], v[6], v[7], s);
+      o.x = fp8_pack4<FMT>(v[0], v[1], v[2], v[3], s);
+      o.y = fp8_pack4<FMT>(v[4], v[5], v[6], v[7], s);
       codes[base + j] = o;
     }
   }
@@ -145,11 +148,15 @@ unsigned stream_grid(int64_t n8, int num_cus) {
 
 hipError_t prepare_quant_kernels() {
   const void* fns[] = {reinterpret_cast<const void*>(&amax_bf16_kernel),
-                       reinterpret_cast<const void*>(&quant_bf16_kernel),
-                       reinterpret_cast<const void*>(&quant_f32_kernel),
+                       reinterpret_cast<const void*>(&quant_bf16_kernel<kFmtE4M3>),
+                       reinterpret_cast<const void*>(&quant_bf16_kernel<kFmtE5M2>),
+                       reinterpret_cast<const void*>(&quant_f32_kernel<kFmtE4M3>),
+                       reinterpret_cast<const void*>(&quant_f32_kernel<kFmtE5M2>),
                        reinterpret_cast<const void*>(&zero_amax_kernel),
-                       reinterpret_cast<const void*>(&quant_rows_kernel<true>),
-                       reinterpret_cast<const void*>(&quant_rows_kernel<false>)};
+                       reinterpret_cast<const void*>(&quant_rows_kernel<true, kFmtE4M3>),
+                       reinterpret_cast<const void*>(&quant_rows_kernel<false, kFmtE4M3>),
+                       reinterpret_cast<const void*>(&quant_rows_kernel<true, kFmtE5M2>),
+                       reinterpret_cast<const void*>(&quant_rows_kernel<false, kFmtE5M2>)};
   for (const void* f : fns) {
     const hipError_t e = prepare_kernel(f, 0);
     if (e != hipSuccess) return e;
@@ -170,33 +177,33 @@ hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cu
   return hipGetLastError();
 }
 
-hipError_t launch_quant_bf16(const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_bf16(int fmt, const void* x, int64_t n, uint32_t* amax, uint8_t* codes,
                              float* scale_out, int num_cus, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  quant_bf16_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
+  auto k = fmt == kFmtE5M2 ? &quant_bf16_kernel<kFmtE5M2> : &quant_bf16_kernel<kFmtE4M3>;
+  k<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
       static_cast<const uint4*>(x), n8, amax, reinterpret_cast<uint2*>(codes), scale_out);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_f32(const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
+hipError_t launch_quant_f32(int fmt, const float* a, int64_t n, uint32_t* amax, uint8_t* codes,
                             int num_cus, hipStream_t stream) {
   const int64_t n8 = n / 8;
-  quant_f32_kernel<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
+  auto k = fmt == kFmtE5M2 ? &quant_f32_kernel<kFmtE5M2> : &quant_f32_kernel<kFmtE4M3>;
+  k<<<stream_grid(n8, num_cus), 256, 0, stream>>>(
       reinterpret_cast<const float4*>(a), n8, amax, reinterpret_cast<uint2*>(codes));
   return hipGetLastError();
 }
 
-hipError_t launch_quant_rows(const void* src, bool bf16, int64_t rows, int C, uint8_t* codes,
-                             float* scales, int num_cus, hipStream_t stream) {
+hipError_t launch_quant_rows(int fmt, const void* src, bool bf16, int64_t rows, int C,
+                             uint8_t* codes, float* scales, int num_cus, hipStream_t stream) {
   int64_t blocks = (rows + 3) / 4;                 // 4 waves (rows) per block
   if (blocks > (int64_t)num_cus * 8) blocks = (int64_t)num_cus * 8;
   const unsigned grid = (unsigned)(blocks > 0 ? blocks : 1);
-  if (bf16)
-    quant_rows_kernel<true><<<grid, 256, 0, stream>>>(src, rows, C / 8,
-                                                      reinterpret_cast<uint2*>(codes), scales);
-  else
-    quant_rows_kernel<false><<<grid, 256, 0, stream>>>(src, rows, C / 8,
-                                                       reinterpret_cast<uint2*>(codes), scales);
+  const bool e5 = fmt == kFmtE5M2;
+  auto k = bf16 ? (e5 ? &quant_rows_kernel<true, kFmtE5M2> : &quant_rows_kernel<true, kFmtE4M3>)
+                : (e5 ? &quant_rows_kernel<false, kFmtE5M2> : &quant_rows_kernel<false, kFmtE4M3>);
+  k<<<grid, 256, 0, stream>>>(src, rows, C / 8, reinterpret_cast<uint2*>(codes), scales);
   return hipGetLastError();
 }
 

@@ -114,11 +114,14 @@ def test_act_quant_validation(L):
 
 def test_act_quant_rows_validation(L):
     p = ctypes.c_void_p(256)
-    assert L.moe_act_quant_fp8_rows(p, 4, 12, p, p, None) == UNSUP             # cols % 8
-    assert L.moe_act_quant_fp8_rows(ctypes.c_void_p(258), 4, 16, p, p, None) == UNSUP
-    assert L.moe_act_quant_fp8_rows(p, 4, 16, p, None, None) == NULL
-    assert L.moe_act_quant_fp8_rows(p, -1, 16, p, p, None) == SHAPE
-    assert L.moe_act_quant_fp8_rows(None, 0, 16, None, None, None) == OK      # no rows
+    E4, E5 = binding.MOE_FP8_E4M3, binding.MOE_FP8_E5M2
+    assert L.moe_act_quant_fp8_rows(p, 4, 12, E4, p, p, None) == UNSUP         # cols % 8
+    assert L.moe_act_quant_fp8_rows(ctypes.c_void_p(258), 4, 16, E5, p, p, None) == UNSUP
+    assert L.moe_act_quant_fp8_rows(p, 4, 16, binding.MOE_BF16, p, p, None) == UNSUP
+    assert L.moe_act_quant_fp8_rows(p, 4, 16, 9, p, p, None) == UNSUP          # no such format
+    assert L.moe_act_quant_fp8_rows(p, 4, 16, E4, p, None, None) == NULL
+    assert L.moe_act_quant_fp8_rows(p, -1, 16, E4, p, p, None) == SHAPE
+    assert L.moe_act_quant_fp8_rows(None, 0, 16, E5, None, None, None) == OK  # no rows
 
 
 def _args(**kw):
@@ -146,6 +149,8 @@ def test_fused_validation(L):
     assert _fwd(L, I=40) == UNSUP           # I % 16
     assert _fwd(L, E=2048, K=4) == UNSUP
     assert _fwd(L, wdtype=7) == UNSUP
+    assert _fwd(L, wdtype=2, workspace_bytes=16) == WS        # E5M2 is a weight type
+    assert _fwd(L, wdtype=2, w2_scale=None) == NULL           # and needs scales
     assert _fwd(L, x=None) == NULL
     assert _fwd(L, w13_scale=None) == NULL          # fp8 needs scales
     assert _fwd(L, out=4097) == UNSUP               # misaligned

@@ -143,9 +143,10 @@ def test_act_quant_zeros():
     _check_quant(torch.zeros(4, 64, dtype=torch.bfloat16))
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("shape", [(1, 4096), (5, 7168), (64, 7168), (4096, 7168), (3, 8),
                                    (300, 1040)])
-def test_act_quant_rows_bit_exact(shape):
+def test_act_quant_rows_bit_exact(shape, fmt):
     """Per-row codes and scales against the oracle's row quantiser; rows of
     very different magnitude (including an all-zero row and one whose values
     fall into the E4M3 subnormal range of a shared scale)."""
@@ -154,10 +155,10 @@ def test_act_quant_rows_bit_exact(shape):
     x = torch.randn(*shape, generator=g) * mag
     x[shape[0] // 2] = 0.0
     x = x.to(torch.bfloat16)
-    say("act_quant rows", shape)
-    codes, scales = mm.act_quant_fp8_rows(x.to(DEV))
+    say("act_quant rows", shape, fmt)
+    codes, scales = mm.act_quant_fp8_rows(x.to(DEV), fmt)
     torch.cuda.synchronize()
-    rc, rs = ofp8.quantize_rows(np_f32(x))
+    rc, rs = ofp8.quantize_rows(np_f32(x), fmt)
     assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32))
     got = codes.cpu().numpy()
     assert np.array_equal(got, rc), int((got != rc).sum())
@@ -168,16 +169,22 @@ def test_act_quant_rows_bit_exact(shape):
 _WCACHE = {}
 
 
+# Weight kinds of the fused tests: bf16; E4M3 ("fp8") or E5M2 ("fp8e5") codes
+# with one scale per expert tensor; "...row": one scale per weight row (and the
+# layer then takes one scale per activation row).
+FP8_KINDS = {"fp8": ("e4m3", "tensor"), "fp8row": ("e4m3", "row"),
+             "fp8e5": ("e5m2", "tensor"), "fp8e5row": ("e5m2", "row")}
+
+
 def _weights(cfg, wdtype, gen_dev):
-    """Weights of cfg; wdtype "fp8row" is E4M3 with one scale per weight row
-    (and the layer then takes one scale per activation row)."""
     key = (cfg.H, cfg.I, cfg.E, cfg.K, cfg.weight_std, wdtype, gen_dev)
     if key not in _WCACHE:
         if len(_WCACHE) > 2:
             _WCACHE.clear()
-        rows = wdtype == "fp8row"
-        w = workloads.make_weights(cfg, seed=0, device=gen_dev, wdtype="fp8" if rows else wdtype,
-                                   scales="row" if rows else "tensor")
+        fmt, scales = FP8_KINDS.get(wdtype, ("e4m3", "tensor"))
+        w = workloads.make_weights(cfg, seed=0, device=gen_dev,
+                                   wdtype="fp8" if wdtype in FP8_KINDS else wdtype,
+                                   scales=scales, fp8_format=fmt)
         _WCACHE[key] = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in w.items()}
     return _WCACHE[key]
 
@@ -189,12 +196,13 @@ def run_case(cfg, T, wdtype, tokens=None, logits_kind=None, gen_dev="cpu", seed=
         tk["logits"] = workloads.tie_heavy_logits(T, cfg.E, seed=seed, device=gen_dev)
     tk = {k: v.to(DEV) for k, v in tk.items()}
     say("fused", cfg.name, dict(T=T, H=cfg.H, I=cfg.I, E=cfg.E, K=cfg.K), wdtype, logits_kind)
-    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"))
+    fmt, scales = FP8_KINDS.get(wdtype, ("e4m3", "tensor"))
+    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"),
+                    fp8_format=fmt)
     out, ids, _ = m(tk["x"], tk["logits"], return_topk=True)
     torch.cuda.synchronize()
     ref, parts = omoe.moe_forward(K=cfg.K, tokens=tokens, return_parts=True, workers=WORKERS,
-                                  act_scales="row" if wdtype == "fp8row" else "tensor",
-                                  **oracle_inputs(w, tk))
+                                  act_scales=scales, **oracle_inputs(w, tk))
     assert np.array_equal(ids.cpu().numpy(), parts["ids"])
     got = np_f32(out)
     if tokens is not None:
@@ -202,9 +210,9 @@ def run_case(cfg, T, wdtype, tokens=None, logits_kind=None, gen_dev="cpu", seed=
     err = rel_err(got, ref)
     assert np.isfinite(got).all()
     say("  rel err", err)
-    if wdtype == "fp8row":
+    if wdtype in FP8_KINDS and wdtype != "fp8":
         sel = np.arange(T) if tokens is None else np.asarray(tokens)
-        allow = near_tie_allowance(parts, w, cfg, sel)
+        allow = near_tie_allowance(parts, w, cfg, sel, fmt)
         excess = np.abs(got.astype(np.float64) - ref) - TOL * np.abs(ref).max()
         say("  near-tie allowance used at", int((excess > 0).sum()), "elements; max allowance",
             float(allow.max() / max(np.abs(ref).max(), 1e-30)))
@@ -229,10 +237,11 @@ def run_case(cfg, T, wdtype, tokens=None, logits_kind=None, gen_dev="cpu", seed=
 NEAR_TIE = 2.0 ** -13
 
 
-def near_tie_allowance(parts, w, cfg, tokens):
+def near_tie_allowance(parts, w, cfg, tokens, fmt="e4m3"):
     """[len(tokens), H] bound on the output change that near-tie intermediate
-    codes can cause by rounding to the other neighbour (per-row scales)."""
-    grid = np.unique(np.abs(ofp8.decode(np.arange(256, dtype=np.uint8))))
+    codes can cause by rounding to the other neighbour."""
+    fmax = ofp8.fp8_max(fmt)
+    grid = np.unique(np.abs(ofp8.decode(np.arange(256, dtype=np.uint8), fmt)))
     grid = grid[np.isfinite(grid)]
     row_of = {int(t): r for r, t in enumerate(tokens)}
     allow = np.zeros((len(tokens), cfg.H))
@@ -240,15 +249,17 @@ def near_tie_allowance(parts, w, cfg, tokens):
     for r, (t, k) in enumerate(parts["a_pairs"]):
         if t not in row_of:
             continue
-        s = np.float64(parts["s_a"][r])
+        s_a = np.asarray(parts["s_a"], dtype=np.float64)
+        s = s_a if s_a.ndim == 0 else s_a[r]
         v = np.abs(parts["a_f32"][r].astype(np.float64)) / s
         j = np.clip(np.searchsorted(grid, v), 1, grid.size - 1)
         lo, hi = grid[j - 1], grid[j]
-        near = np.abs(v - (lo + hi) / 2) <= NEAR_TIE * 448.0
+        near = np.abs(v - (lo + hi) / 2) <= NEAR_TIE * fmax
         if not near.any():
             continue
         e = int(parts["ids"][t, k])
-        w2 = ofp8.decode(np_u8(w["w2"][e])) * np_f32(w["w2_scale"][e]).astype(np.float64)[:, None]
+        sw = np_f32(w["w2_scale"][e]).astype(np.float64)
+        w2 = ofp8.decode(np_u8(w["w2"][e]), fmt) * (sw[:, None] if sw.ndim else sw)
         step = (hi - lo)[near] * s
         allow[row_of[t]] += abs(wts[t, k]) * (np.abs(w2[:, near]) @ step)
     return allow
@@ -257,13 +268,13 @@ def near_tie_allowance(parts, w, cfg, tokens):
 TINY = workloads.CONFIGS["tiny"]
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5", "fp8e5row"])
 @pytest.mark.parametrize("T", [1, 4, 5, 16, 17, 33, 64, 100, 300])
 def test_fused_tiny(T, wdtype):
     run_case(TINY, T, wdtype)
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("over", [
     dict(H=144, I=48, E=6, K=3),         # ragged chunk tails in both GEMMs
     dict(H=272, I=80, E=5, K=5),         # K = E
@@ -276,7 +287,7 @@ def test_fused_shapes(over, wdtype):
         run_case(cfg, T, wdtype)
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 def test_fused_tie_heavy_routing(wdtype):
     run_case(TINY, 50, wdtype, logits_kind="ties")
 
@@ -296,19 +307,19 @@ def test_fused_bf16_decode(T):
     run_case(workloads.CONFIGS["bf16_decode"], T, "bf16", gen_dev=DEV)
 
 
-@pytest.mark.parametrize("wdtype", ["fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("T", [1, 8, 32, 64])
 def test_fused_fp8_decode(T, wdtype):
     run_case(workloads.CONFIGS["fp8_decode"], T, wdtype, gen_dev=DEV)
 
 
-@pytest.mark.parametrize("wdtype", ["fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
 def test_fused_fp8_tp8_slice(T, wdtype):
     run_case(workloads.CONFIGS["fp8_tp8_slice"], T, wdtype, gen_dev=DEV)
 
 
-@pytest.mark.parametrize("wdtype", ["fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["fp8", "fp8row", "fp8e5"])
 def test_fused_fp8_prefill_zipf_sampled(wdtype):
     cfg = workloads.CONFIGS["fp8_prefill_zipf"]
     tokens = np.random.default_rng(0).choice(4096, 24, replace=False)
@@ -317,7 +328,7 @@ def test_fused_fp8_prefill_zipf_sampled(wdtype):
 
 # ------------------------------------------------------------------ determinism
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 7),   # front launch (T <= 16)
     (dict(H=2048, I=1040, E=16, K=4), 40),  # router, act quant and align launches
@@ -329,7 +340,8 @@ def test_fused_graph_replay_matches_eager(over, T, wdtype):
     records no memset and allocates nothing, so its launches replay as is)."""
     cfg = replace(TINY, name="graph", **over)
     w = _weights(cfg, wdtype, "cpu")
-    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"))
+    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"),
+                    fp8_format=FP8_KINDS.get(wdtype, ("e4m3",))[0])
     tk = workloads.make_tokens(cfg, T, seed=5)
     x, lg = tk["x"].to(DEV), tk["logits"].to(DEV)
     other = workloads.make_tokens(cfg, T, seed=6)
@@ -350,7 +362,7 @@ def test_fused_graph_replay_matches_eager(over, T, wdtype):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 7),   # row tails in both products
     (dict(H=144, I=48, E=6, K=3), 40),
@@ -363,7 +375,8 @@ def test_fused_run_to_run_bit_identical(over, T, wdtype):
     w = _weights(cfg, wdtype, "cpu")
     tk = workloads.make_tokens(cfg, T, seed=3)
     x, lg = tk["x"].to(DEV), tk["logits"].to(DEV)
-    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"))
+    m = mm.FusedMoE(w["w13"], w["w2"], cfg.K, w.get("w13_scale"), w.get("w2_scale"),
+                    fp8_format=FP8_KINDS.get(wdtype, ("e4m3",))[0])
     say("determinism", over, T, wdtype)
     first = m(x, lg).clone()
     for _ in range(7):
@@ -372,7 +385,7 @@ def test_fused_run_to_run_bit_identical(over, T, wdtype):
         assert torch.equal(first.view(torch.int16), again.view(torch.int16))
 
 
-@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row"])
+@pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("over,T", [
     (dict(H=2048, I=1040, E=16, K=4), 512),   # tiled experts + small ones, column and row tails
     (dict(H=1152, I=320, E=32, K=6), 700),
