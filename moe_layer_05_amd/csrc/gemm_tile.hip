@@ -113,10 +113,11 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   // Persistent: one workgroup per compute unit walks a list of tiles.  The
   // routed blocks are cut into 8 contiguous ranges, one per XCD (workgroups
   // are handed to the XCDs in turn, blockIdx & 7).  An XCD's tiles are walked
-  // in panels of 4 blocks x 8 column tiles and its workgroups take them in
-  // turn, so the 32 tiles running at once on an XCD read 4 token slices and 8
-  // weight slices per k-step from its L2 (a 2 x 16 arrangement would read 18).
-  constexpr int kPB = 4, kPN = 8;
+  // in panels of 8 blocks x 4 column tiles and its workgroups take them in
+  // turn, so the 32 tiles running at once on an XCD read 8 token slices and 4
+  // weight slices per k-step from its L2 (measured 1.5% faster per prefill
+  // step than 4 x 8 with the weights loaded through the caches).
+  constexpr int kPB = 8, kPN = 4;
   const int nb = p.num_post_pad[0] / kTN;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, nj = gridDim.x >> 3;
   const int b0 = (xcd * nb) >> 3, b1 = ((xcd + 1) * nb) >> 3;
@@ -191,9 +192,11 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     const uint32_t o = (!tail || off + gq < (uint32_t)row_bytes) ? off + gq : 0u;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
+      // weights through the caches: the other token blocks of the panel
+      // read the same weight slice
       __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + o),
                                        (lds_void*)(a_lds + stage * kStageBytes + i * 1024), 16,
-                                       0, 2);
+                                       0, 0);
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + o),
