@@ -24,10 +24,12 @@ Arithmetic is float64 unless a step turns a float into an integer (an FP8
 code); there both sides decide in float32, the precision of the device.
 
 Modules:
-    fp8    -- OCP E4M3 ("fn") decode table, encoder, per-tensor quantiser,
-              bfloat16 round-to-nearest-even.
+    fp8    -- OCP E4M3 ("fn") and E5M2 decode tables and encoders, the
+              per-tensor and per-row quantisers, bfloat16
+              round-to-nearest-even.
     moe    -- router (top-k), align (stable counting sort padded to a block
-              size), the sparse layer, and the dense masked formulation.
+              size), the sparse layer (bf16, or FP8 with per-tensor or
+              per-row scales), and the dense masked formulation.
 """
 
 from . import fp8, moe  # noqa: F401
