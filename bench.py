@@ -270,15 +270,27 @@ def oracle_and_parity(cfg, m, w, tk, budget, scales="tensor", fmt="e4m3"):
             break
         n = min(T, 2 * n)
     n, dt, ref, parts, x, lg = last
+    # a whole batch that runs in a few seconds is run again until the sample
+    # holds about half the budget of oracle work; the rate is over all runs
+    runs, total = 1, dt
+    if n >= T:
+        xh, lh = x.float().cpu().numpy(), lg.cpu().numpy()
+        while total < budget / 2 and runs < 16:
+            t0 = time.perf_counter()
+            omoe.moe_forward(xh, lh, K=cfg.K, act_scales=scales if fp8 else "tensor",
+                             fp8_format=fmt, **kw)
+            total += time.perf_counter() - t0
+            runs += 1
+        log(f"oracle: {runs} runs of the {n}-token batch, {total:.2f} s")
     out, ids, _ = m(x, lg, return_topk=True)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     err = float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
     ids_ok = bool(np.array_equal(ids.cpu().numpy(), parts["ids"]))
-    cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": blas_threads(),
+    cpu = {"value": round(n * runs / total, 3), "unit": "tokens/s", "cores": blas_threads(),
            "kind": "oracle",
            "sample": f"first {n} of the {T} tokens run as their own batch through the "
-                     f"float64 numpy oracle (same weights), {dt:.2f} s"}
+                     f"float64 numpy oracle (same weights), {runs} run(s), {total:.2f} s"}
     parity = {"tokens": n, "ids_bit_exact": ids_ok, "max_rel_err": err, "tol": 1e-2,
               "ok": ids_ok and err <= 1e-2}
     return cpu, parity
