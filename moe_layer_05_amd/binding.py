@@ -214,7 +214,8 @@ class FusedMoE:
     tensor activation scales) or [E, 2I] / [E, H] (one per weight row, and
     per row activation scales); ``fp8_format`` says whether the codes are
     E4M3 or E5M2.  The workspace is a torch buffer grown on demand and reused
-    across calls (the library allocates nothing)."""
+    across calls on the same stream (the library allocates nothing); calls on
+    different streams get separate workspaces, so they may overlap."""
 
     def __init__(self, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True,
                  fp8_format="e4m3"):
@@ -244,9 +245,22 @@ class FusedMoE:
                 raise ValueError(f"scales must be {want13} and {want2}")
         self.w13_scale = w13_scale
         self.w2_scale = w2_scale
-        self._ws = None
+        self._ws = {}                                # (device, stream handle) -> buffer
 
     def args(self, x, logits, out, ids=None, wts=None):
+        # the library trusts these shapes: a wrong width would be read out of bounds
+        if x.dim() != 2 or x.shape[1] != self.H:
+            raise ValueError(f"x must be [T, {self.H}], got {tuple(x.shape)}")
+        T = x.shape[0]
+        if tuple(logits.shape) != (T, self.E):
+            raise ValueError(f"logits must be [{T}, {self.E}], got {tuple(logits.shape)}")
+        if tuple(out.shape) != (T, self.H):
+            raise ValueError(f"out must be [{T}, {self.H}], got {tuple(out.shape)}")
+        for name, t, dt in (("topk_ids", ids, torch.int32), ("topk_weights", wts, torch.float32)):
+            if t is not None:
+                _dev(t, dt, name)
+                if tuple(t.shape) != (T, self.K):
+                    raise ValueError(f"{name} must be [{T}, {self.K}]")
         a = FusedArgs()
         a.wdtype = self.wdtype
         a.fp8_scales = MOE_SCALES_ROW if self.rows else MOE_SCALES_TENSOR
@@ -271,11 +285,18 @@ class FusedMoE:
         a.T, a.H, a.I, a.E, a.K = T, self.H, self.I, self.E, self.K
         return int(lib().moe_fused_workspace_bytes(ctypes.byref(a)))
 
-    def workspace(self, T, device):
+    def workspace(self, T, device, stream=None):
+        """The workspace for calls on ``stream`` (default: the current one),
+        grown to T tokens if needed."""
         need = self.workspace_bytes(T)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-        return self._ws
+        st = stream if stream is not None else torch.cuda.current_stream(device)
+        key = (str(device), st.cuda_stream)
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < need:
+            with torch.cuda.stream(st):
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+            self._ws[key] = ws
+        return ws
 
     def __call__(self, x, logits, out=None, return_topk=False, stream=None, events=None):
         """out [T, H] bfloat16 of x [T, H] bfloat16 and logits [T, E] float32.
@@ -291,8 +312,8 @@ class FusedMoE:
         if return_topk:
             ids = torch.empty(T, self.K, dtype=torch.int32, device=x.device)
             wts = torch.empty(T, self.K, dtype=torch.float32, device=x.device)
-        ws = self.workspace(T, x.device)
         a = self.args(x, logits, out, ids, wts)
+        ws = self.workspace(T, x.device, stream)
         a.workspace = ws.data_ptr()
         a.workspace_bytes = ws.numel()
         if events is None:

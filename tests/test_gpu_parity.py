@@ -287,6 +287,25 @@ def test_fused_shapes(over, wdtype):
         run_case(cfg, T, wdtype)
 
 
+def test_fused_rejects_mismatched_shapes():
+    """The binding checks every tensor against the layer's H, E and K before
+    the library (which trusts them) is called."""
+    w = _weights(TINY, "bf16", "cpu")
+    m = mm.FusedMoE(w["w13"], w["w2"], TINY.K)
+    x = torch.zeros(3, TINY.H, dtype=torch.bfloat16, device=DEV)
+    lg = torch.zeros(3, TINY.E, dtype=torch.float32, device=DEV)
+    bad = [
+        (torch.zeros(3, TINY.H + 16, dtype=torch.bfloat16, device=DEV), lg, None),
+        (x, torch.zeros(3, TINY.E + 1, dtype=torch.float32, device=DEV), None),
+        (x, torch.zeros(4, TINY.E, dtype=torch.float32, device=DEV), None),
+        (x, lg, torch.empty(3, TINY.H - 16, dtype=torch.bfloat16, device=DEV)),
+    ]
+    for xx, ll, oo in bad:
+        with pytest.raises(ValueError):
+            m(xx, ll, out=oo)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 def test_fused_tie_heavy_routing(wdtype):
     run_case(TINY, 50, wdtype, logits_kind="ties")
@@ -348,17 +367,19 @@ def test_fused_graph_replay_matches_eager(over, T, wdtype):
     xo, lgo = other["x"].to(DEV), other["logits"].to(DEV)
     say("graph replay", over, T, wdtype)
     ref = m(x, lg).clone()
-    m.workspace(T, x.device)                 # sized before capture
+    cs = torch.cuda.Stream()
+    m.workspace(T, x.device, cs)             # the capture stream's, sized before capture
     out = torch.empty_like(ref)
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=cs):
         m(x, lg, out=out)
     torch.cuda.synchronize()
     for _ in range(3):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
-        m(xo, lgo)                           # eager work on the same workspace
+        m(xo, lgo, stream=cs)                # eager work on the same workspace
         torch.cuda.synchronize()
 
 
