@@ -74,6 +74,11 @@ int64_t max_blocks(int64_t P, int E, int bm) {
 // weight-streaming kernels.
 constexpr int kTileThreshold = 16;
 
+// Largest x (bytes) whose amax the router launch reduces itself (kAmaxSlots
+// workgroups); measured: 512 KB (T = 64, H = 4096) saves a launch, 58.7 MB
+// (T = 4096, H = 7168) is slower than the many-workgroup amax launch.
+constexpr int64_t kRouterAmaxMaxBytes = 8 << 20;
+
 struct FusedLayout {
   size_t ids, wts, sorted, bexp, npp, rank, scal, srow, qx, a, qa, dw, ascr, total;
   size_t sorted_t, bexp_t, npp_t;     // tiled layout (prefill)
@@ -329,16 +334,28 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
   } else {
-    // a1 (also clears the amax slots of x and a for this call)
-    if (e == hipSuccess)
-      e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x,
-                        fp8 && !rows ? 2 : 0, stream);
+    // a1.  Per-tensor FP8 with a small x: the same launch clears the amax
+    // slots of a and stores the amax of x in the slots of x (a0's first
+    // half, one launch less).  A large x (prefill) needs more workgroups than
+    // that launch adds: the router clears both amax blocks and a launch of
+    // its own reduces x.
+    const bool tensor_fp8 = fp8 && !rows;
+    const bool amax_in_router = tensor_fp8 && T * (int64_t)H * 2 <= kRouterAmaxMaxBytes;
+    if (e == hipSuccess) {
+      if (amax_in_router)
+        e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_a, 1,
+                          stream, a->x, T * H, amax_x);
+      else
+        e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x,
+                          tensor_fp8 ? 2 : 0, stream);
+    }
     // a0
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
     if (e == hipSuccess && rows) {
       e = launch_quant_rows(fmt, a->x, true, T, H, qx, sx, cus, stream);
     } else if (fp8) {
-      if (e == hipSuccess) e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
+      if (e == hipSuccess && !amax_in_router)
+        e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
       if (e == hipSuccess)
         e = launch_quant_bf16(fmt, a->x, T * H, amax_x, qx, nullptr, cus, stream);
     }

@@ -48,9 +48,14 @@ struct DecodeShape {
   int ra, groups, splits;
 };
 
+// a1; zero_amax: n_amax consecutive amax blocks cleared by the launch.  With
+// x set (n bfloat16 values, n % 8 == 0), kAmaxSlots more workgroups of the
+// same launch store the amax of x into the slots of amax_x, one each (a0's
+// first half: every slot is written, none needs clearing).
 hipError_t launch_router(const float* logits, int64_t T, int E, int K, int renorm,
                          int32_t* ids, float* wts, uint32_t* zero_amax, int n_amax,
-                         hipStream_t stream);
+                         hipStream_t stream, const void* x = nullptr, int64_t n = 0,
+                         uint32_t* amax_x = nullptr);
 
 size_t align_lds_bytes(int E);
 hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
