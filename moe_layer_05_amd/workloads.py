@@ -175,3 +175,60 @@ def tie_heavy_logits(T, E, seed=0, device="cpu", levels=4):
     g = _gen(device, seed, 3, T)
     v = torch.randint(0, levels, (T, E), generator=g, device=device)
     return v.to(torch.float32)
+
+
+# ---------------------------------------------------------------------------
+# The attention-side kernel the pages name next to the MoE layer: inverse
+# rotary embedding of attention heads followed by per-head FP8 quantisation,
+# called with a token count that changes from call to call (toolboxkart.tech
+# page, section 3; aib.vote page, fourth paragraph).  The pages give no model;
+# the shapes stand in for one GPU's share at 8-way tensor parallelism of a
+# 128-head attention with 128-feature heads (16 heads per GPU), fully rotary
+# (half layout), and a partly rotary variant (64 of 192 features, interleaved
+# pairs).  Positions: a decode batch draws them at random below max_pos; a
+# prefill batch is one sequence, positions 0..T-1.
+
+@dataclass(frozen=True)
+class RopeConfig:
+    name: str
+    NH: int                      # heads per token
+    D: int                       # features per head
+    R: int                       # rotated features (the rest pass through)
+    interleaved: bool            # pairs (2i, 2i+1) instead of (i, i + R/2)
+    max_pos: int
+    base: float
+    Ts: tuple
+
+
+ROPE_CONFIGS = {
+    "inv_rope_tp8": RopeConfig("inv_rope_tp8", NH=16, D=128, R=128, interleaved=False,
+                               max_pos=32768, base=10000.0, Ts=(1, 16, 64, 4096)),
+    "inv_rope_partial": RopeConfig("inv_rope_partial", NH=16, D=192, R=64, interleaved=True,
+                                   max_pos=32768, base=10000.0, Ts=(1, 16, 64, 4096)),
+}
+
+_ROLE_HEADS = 4
+
+
+def rope_table(max_pos, R, base=10000.0):
+    """[max_pos, R] float32 table: cos of the R/2 angles p * base^(-2i/R) of
+    position p, then their sin (computed in float64, rounded once)."""
+    i = torch.arange(R // 2, dtype=torch.float64)
+    inv_freq = base ** (-2.0 * i / R)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv_freq[None, :]
+    return torch.cat([ang.cos(), ang.sin()], dim=1).to(torch.float32).contiguous()
+
+
+def make_heads(cfg, T, seed=0, device="cpu", prefill=None):
+    """x [T, NH, D] bfloat16 ~ N(0, 1) and positions [T] int64 of ``cfg``:
+    one sequence 0..T-1 when ``prefill`` (default: T > 64), else random
+    positions below max_pos (a decode batch of independent sequences)."""
+    g = _gen(device, seed, _ROLE_HEADS, T)
+    x = torch.randn(T, cfg.NH, cfg.D, generator=g, device=device).to(torch.bfloat16)
+    if prefill is None:
+        prefill = T > 64
+    if prefill:
+        pos = torch.arange(T, dtype=torch.int64, device=device)
+    else:
+        pos = torch.randint(0, cfg.max_pos, (T,), generator=g, device=device, dtype=torch.int64)
+    return {"x": x, "positions": pos}

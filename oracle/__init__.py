@@ -30,6 +30,9 @@ Modules:
     moe    -- router (top-k), align (stable counting sort padded to a block
               size), the sparse layer (bf16, or FP8 with per-tensor or
               per-row scales), and the dense masked formulation.
+    rope   -- inverse rotary position embedding of attention heads followed
+              by one FP8 scale per (token, head) (the pages' attention-side
+              kernel with a variable token count).
 """
 
-from . import fp8, moe  # noqa: F401
+from . import fp8, moe, rope  # noqa: F401
