@@ -197,9 +197,10 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
     workers experts evaluated concurrently (same arithmetic, less wall time).
 
     Returns out [len(tokens), H] float32 holding bfloat16 values; with
-    ``return_parts`` also a dict with y (before rounding), ids, weights and,
-    in FP8 mode, the activation scales and the intermediate rows before their
-    quantisation (a_f32, one row per (t, k) in a_pairs).
+    ``return_parts`` also a dict with y (before rounding), ids, weights, the
+    intermediate rows a (in ``dtype``, one row per (t, k) in a_pairs) and, in
+    FP8 mode, the activation scales and the float32 rows that were quantised
+    (a_f32).
 
     In FP8 mode the intermediate scale needs every routed pair, so gate/up runs
     for all pairs; the down projection and the combine run for ``tokens`` only.
@@ -245,15 +246,17 @@ def moe_forward(x, logits, w13, w2, K, wdtype="float", w13_scale=None,
         for r, (t, k) in enumerate(tk):
             a[(int(t), int(k))] = ae[r]
 
-    if fp8_mode and a:
+    if a:
         keys = sorted(a)
-        amat = np.stack([a[kk] for kk in keys]).astype(np.float32)
+        parts["a_pairs"] = keys              # (t, k) of each row of a / a_f32 / s_a
+        parts["a"] = np.stack([a[kk] for kk in keys])   # before any quantisation
+    if fp8_mode and a:
+        amat = parts["a"].astype(np.float32)
         qa, s_a = act_quant(amat, act_scales, fmt)
         ah = _dequant(qa, s_a, act_scales, fmt)
         for r, kk in enumerate(keys):
             a[kk] = ah[r].astype(dtype)
         parts["s_a"] = s_a
-        parts["a_pairs"] = keys              # (t, k) of each row of a_f32 / s_a
         parts["a_f32"] = amat                # the values that were quantised
 
     # down projection and routing-weighted combine

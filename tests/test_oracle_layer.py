@@ -381,3 +381,30 @@ def test_e5m2_and_e4m3_agree_within_their_precision():
     y5 = moe.moe_forward(K=cfg.K, **oracle_inputs(w5, tk))
     rel = np.abs(y5 - y4).max() / np.abs(y4).max()
     assert 1e-3 < rel < 0.2
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_token_subset_keeps_the_tensor_scale(fmt):
+    """With one intermediate scale per tensor, s_a is taken over every routed
+    pair of the call even when only some tokens are evaluated: the rows of a
+    token subset equal those rows of the full call bit for bit, with the same
+    s_a.  The subset leaves out the token that holds amax|a|, so taking s_a
+    over the sampled pairs only would change it (checked below)."""
+    cfg = workloads.CONFIGS["tiny"]
+    T = 9
+    w = workloads.make_weights(cfg, seed=0, wdtype="fp8", fp8_format=fmt)
+    tk = workloads.make_tokens(cfg, T, seed=0)
+    kw = oracle_inputs(w, tk)
+    out, full = moe.moe_forward(K=cfg.K, return_parts=True, **kw)
+    amax_row = int(np.abs(full["a_f32"]).max(axis=1).argmax())
+    t_max = full["a_pairs"][amax_row][0]
+    sub = [t for t in (7, 3, 1, 5) if t != t_max][:3]
+    out_s, part = moe.moe_forward(K=cfg.K, tokens=sub, return_parts=True, **kw)
+    assert part["s_a"] == full["s_a"]
+    assert np.array_equal(part["a_f32"], full["a_f32"])
+    assert np.array_equal(out_s, out[sub])
+    assert np.allclose(part["y"], full["y"][sub], rtol=1e-13, atol=1e-15)
+    # the subset's own pairs have a smaller amax: a scale over them would differ
+    rows = [r for r, (t, _) in enumerate(full["a_pairs"]) if t in sub]
+    s_sub = fp8.per_tensor_scale(full["a_f32"][rows], fmt)
+    assert s_sub != full["s_a"]
