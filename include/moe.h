@@ -220,6 +220,51 @@ typedef struct {
  * are not read). 0 when the shape is invalid. */
 size_t moe_fused_workspace_bytes(const moe_fused_args* args);
 
+/*
+ * Where moe_fused_forward keeps each intermediate result inside the caller's
+ * workspace, for callers (tests, debuggers) that inspect the steps of a call
+ * after it has completed on its stream and before the workspace is reused.
+ * Each field is a byte offset from the workspace start, or MOE_NO_SECTION
+ * when the call has no such result (for its weight type, scale mode or size).
+ * Layout of the sections (P = T*K pairs, pair i = t*K + k):
+ *   topk_ids, topk_weights  [T, K] int32 / float32 (used only when the caller
+ *                           passes no topk_ids_out / topk_weights_out)
+ *   sorted_ids, block_expert, num_post_pad  the align layout (as moe_align)
+ *                           with block size block_m over `capacity` entries;
+ *                           when `tiled` is 1 it holds only the experts with
+ *                           fewer than tile_threshold pairs
+ *   tile_sorted_ids, tile_block_expert, tile_num_post_pad  (tiled == 1) the
+ *                           layout of the experts with >= tile_threshold pairs,
+ *                           block size tile_block_m, tile_capacity entries
+ *   x_amax                  uint32: the float bits of amax|x| (FP8, per tensor)
+ *   x_codes                 [T, H] uint8 FP8 codes of x (FP8)
+ *   x_scales                [T] float32 per-row scales of x (FP8, per row)
+ *   a                       [P, I] the intermediate silu(g) * u in pair
+ *                           order: float32 (FP8) or bfloat16 (bf16)
+ *   a_amax                  uint32: the float bits of amax|a| over all pairs
+ *                           (FP8, per tensor)
+ *   a_codes                 [P, I] uint8 FP8 codes of a (FP8)
+ *   a_scales                [P] float32 per-row scales of a (FP8, per row)
+ * Pointers of *args are not read.  Errors: MOE_ERR_NULL, and the shape checks
+ * of moe_fused_forward.
+ */
+#define MOE_NO_SECTION ((size_t)-1)
+typedef struct {
+  size_t total;                  /* == moe_fused_workspace_bytes(args) */
+  int32_t block_m;
+  int32_t tiled;
+  int32_t tile_block_m;
+  int32_t tile_threshold;
+  int64_t capacity;
+  int64_t tile_capacity;
+  size_t topk_ids, topk_weights;
+  size_t sorted_ids, block_expert, num_post_pad;
+  size_t tile_sorted_ids, tile_block_expert, tile_num_post_pad;
+  size_t x_amax, x_codes, x_scales;
+  size_t a, a_amax, a_codes, a_scales;
+} moe_fused_layout;
+moe_status moe_fused_workspace_layout(const moe_fused_args* args, moe_fused_layout* layout);
+
 /* Block size (tokens per expert block) moe_fused_forward uses for this shape;
  * moe_align with this block_m reproduces its layout. */
 int32_t moe_fused_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t K,

@@ -7,7 +7,10 @@ ahead-of-time build (``build``) and the seeded synthetic workloads
 """
 
 from .binding import (  # noqa: F401
+    FusedLayout,
     FusedMoE,
+    NO_SECTION,
+    WorkspacePool,
     MoEError,
     act_quant_fp8,
     act_quant_fp8_rows,

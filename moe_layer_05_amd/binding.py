@@ -55,6 +55,38 @@ class FusedArgs(ctypes.Structure):
     ]
 
 
+NO_SECTION = ctypes.c_size_t(-1).value
+
+
+class FusedLayout(ctypes.Structure):
+    """moe_fused_layout: byte offsets of a call's intermediate results inside
+    its workspace (NO_SECTION where the call has no such result)."""
+    _fields_ = [
+        ("total", ctypes.c_size_t),
+        ("block_m", ctypes.c_int32),
+        ("tiled", ctypes.c_int32),
+        ("tile_block_m", ctypes.c_int32),
+        ("tile_threshold", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("tile_capacity", ctypes.c_int64),
+        ("topk_ids", ctypes.c_size_t),
+        ("topk_weights", ctypes.c_size_t),
+        ("sorted_ids", ctypes.c_size_t),
+        ("block_expert", ctypes.c_size_t),
+        ("num_post_pad", ctypes.c_size_t),
+        ("tile_sorted_ids", ctypes.c_size_t),
+        ("tile_block_expert", ctypes.c_size_t),
+        ("tile_num_post_pad", ctypes.c_size_t),
+        ("x_amax", ctypes.c_size_t),
+        ("x_codes", ctypes.c_size_t),
+        ("x_scales", ctypes.c_size_t),
+        ("a", ctypes.c_size_t),
+        ("a_amax", ctypes.c_size_t),
+        ("a_codes", ctypes.c_size_t),
+        ("a_scales", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 _SIGS = {
@@ -80,6 +112,8 @@ _SIGS = {
     "moe_fused_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(FusedArgs)]),
     "moe_fused_block_m": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int]),
+    "moe_fused_workspace_layout": (ctypes.c_int, [ctypes.POINTER(FusedArgs),
+                                                  ctypes.POINTER(FusedLayout)]),
     "moe_fused_forward": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p]),
     "moe_fused_forward_timed": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p,
                                                ctypes.c_void_p]),
@@ -206,6 +240,47 @@ def fused_block_m(T, H, I, E, K, fp8):
     return int(lib().moe_fused_block_m(T, H, I, E, K, MOE_FP8_E4M3 if fp8 else MOE_BF16))
 
 
+class WorkspacePool:
+    """Workspaces of one layer, one per (device, stream) key, so calls
+    enqueued on different streams never share scratch memory.  At most
+    ``max_entries`` are kept: taking a workspace for a new key when the pool is
+    full drops the least recently used one (a dropped buffer returns to
+    torch's caching allocator, which reuses its memory only for work ordered
+    after the calls already enqueued on that buffer's stream).  ``alloc(nbytes,
+    key, ctx)`` makes a buffer with ``numel()`` bytes; ``ctx`` is passed through
+    from ``get``."""
+
+    def __init__(self, alloc, max_entries=4):
+        if max_entries < 1:
+            raise ValueError("max_entries must be >= 1")
+        self.alloc = alloc
+        self.max_entries = max_entries
+        self._bufs = {}                              # key -> buffer, oldest use first
+
+    def get(self, key, nbytes, ctx=None):
+        buf = self._bufs.pop(key, None)
+        if buf is None or buf.numel() < nbytes:
+            buf = None                               # drop a too-small buffer first
+            while len(self._bufs) >= self.max_entries:
+                self._bufs.pop(next(iter(self._bufs)))
+            buf = self.alloc(max(nbytes, 256), key, ctx)
+        self._bufs[key] = buf                        # most recently used last
+        return buf
+
+    def release(self, key=None):
+        """Drop the workspace of ``key``, or every workspace."""
+        if key is None:
+            self._bufs.clear()
+        else:
+            self._bufs.pop(key, None)
+
+    def __len__(self):
+        return len(self._bufs)
+
+    def keys(self):
+        return list(self._bufs)
+
+
 class FusedMoE:
     """The fused layer forward bound to fixed weights.
 
@@ -215,10 +290,12 @@ class FusedMoE:
     per row activation scales); ``fp8_format`` says whether the codes are
     E4M3 or E5M2.  The workspace is a torch buffer grown on demand and reused
     across calls on the same stream (the library allocates nothing); calls on
-    different streams get separate workspaces, so they may overlap."""
+    different streams get separate workspaces, so they may overlap.  At most
+    ``max_workspaces`` are kept (least recently used dropped first);
+    ``release_workspaces()`` drops them all."""
 
     def __init__(self, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True,
-                 fp8_format="e4m3"):
+                 fp8_format="e4m3", max_workspaces=4):
         self.fp8 = w13.dtype == torch.uint8
         if fp8_format not in _FP8_WDTYPE:
             raise ValueError(f"fp8_format must be one of {sorted(_FP8_WDTYPE)}")
@@ -245,7 +322,7 @@ class FusedMoE:
                 raise ValueError(f"scales must be {want13} and {want2}")
         self.w13_scale = w13_scale
         self.w2_scale = w2_scale
-        self._ws = {}                                # (device, stream handle) -> buffer
+        self._ws = WorkspacePool(self._alloc_ws, max_workspaces)
 
     def args(self, x, logits, out, ids=None, wts=None):
         # the library trusts these shapes: a wrong width would be read out of bounds
@@ -278,25 +355,40 @@ class FusedMoE:
         a.topk_weights_out = wts.data_ptr() if wts is not None else None
         return a
 
-    def workspace_bytes(self, T):
+    def _shape_args(self, T):
         a = FusedArgs()
         a.wdtype = self.wdtype
         a.fp8_scales = MOE_SCALES_ROW if self.rows else MOE_SCALES_TENSOR
         a.T, a.H, a.I, a.E, a.K = T, self.H, self.I, self.E, self.K
-        return int(lib().moe_fused_workspace_bytes(ctypes.byref(a)))
+        a.renormalize = int(bool(self.renormalize))
+        return a
+
+    def workspace_bytes(self, T):
+        return int(lib().moe_fused_workspace_bytes(ctypes.byref(self._shape_args(T))))
+
+    def workspace_layout(self, T):
+        """FusedLayout of a call with T tokens (offsets into its workspace)."""
+        out = FusedLayout()
+        _check(lib().moe_fused_workspace_layout(ctypes.byref(self._shape_args(T)),
+                                                ctypes.byref(out)),
+               "moe_fused_workspace_layout")
+        return out
+
+    @staticmethod
+    def _alloc_ws(nbytes, key, st):
+        with torch.cuda.stream(st):
+            return torch.empty(nbytes, dtype=torch.uint8, device=key[0])
 
     def workspace(self, T, device, stream=None):
         """The workspace for calls on ``stream`` (default: the current one),
         grown to T tokens if needed."""
         need = self.workspace_bytes(T)
         st = stream if stream is not None else torch.cuda.current_stream(device)
-        key = (str(device), st.cuda_stream)
-        ws = self._ws.get(key)
-        if ws is None or ws.numel() < need:
-            with torch.cuda.stream(st):
-                ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-            self._ws[key] = ws
-        return ws
+        return self._ws.get((str(device), st.cuda_stream), need, st)
+
+    def release_workspaces(self):
+        """Drop every workspace this layer holds (the next call allocates)."""
+        self._ws.release()
 
     def __call__(self, x, logits, out=None, return_topk=False, stream=None, events=None):
         """out [T, H] bfloat16 of x [T, H] bfloat16 and logits [T, E] float32.

@@ -3,6 +3,7 @@
 // allocated and nothing synchronises the host.
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "moe.h"
 #include "device_common.hpp"
@@ -18,18 +19,30 @@ constexpr int kMaxK = 64;
 size_t round_up(size_t x) { return (x + kAlignBytes - 1) / kAlignBytes * kAlignBytes; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Every kernel of the library resolved once per device, at the first call
-// on it (so no later call, at whatever token count, pays a kernel's first
-// lookup).  Returns the first error.
+// Per-device state, filled once per device id (any id the runtime reports):
+// every kernel of the library resolved (so no later call, at whatever token
+// count, pays a kernel's first lookup) and the compute-unit count.
+struct DeviceState {
+  bool prepared = false;
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+std::vector<DeviceState> g_dev;   // indexed by device id; guarded by g_dev_mu
+
+DeviceState& device_state(int dev) {
+  if ((size_t)dev >= g_dev.size()) g_dev.resize((size_t)dev + 1);
+  return g_dev[(size_t)dev];
+}
+
+// Resolves every kernel on the current device once; returns the first error.
 hipError_t prepare_all() {
-  static std::mutex mu;
-  static bool done[256] = {false};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 256) return hipSuccess;
-  std::lock_guard<std::mutex> lock(mu);
-  if (done[dev]) return hipSuccess;
+  if (dev < 0) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceState& st = device_state(dev);
+  if (st.prepared) return hipSuccess;
   e = prepare_decode_kernels();
   if (e == hipSuccess) e = prepare_tile_kernels();
   if (e == hipSuccess) e = prepare_router_kernels();
@@ -37,24 +50,24 @@ hipError_t prepare_all() {
   if (e == hipSuccess) e = prepare_front_kernels();
   if (e == hipSuccess) e = prepare_quant_kernels();
   if (e == hipSuccess) e = prepare_combine_kernels();
-  if (e == hipSuccess) done[dev] = true;
+  if (e == hipSuccess) st.prepared = true;
   return e;
 }
 
-// Compute-unit count of the current device, filled once per device.
+// Compute-unit count of the current device (256, MI355X's, when no device
+// can be queried: the host-only size queries then still answer).
 int num_cus() {
-  static std::mutex mu;
-  static int cache[256] = {0};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cache[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceState& st = device_state(dev);
+  if (st.cus == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cache[dev] = n;
+    st.cus = n;
   }
-  return cache[dev];
+  return st.cus;
 }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
@@ -104,7 +117,10 @@ bool use_tiles(int64_t T, int E, int K) {
   return T >= 256 && T * (int64_t)K >= 32LL * E;
 }
 
-FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, bool rows) {
+// Workspace layout of a call; the kernel shapes are chosen for `cus` compute
+// units, the sizes do not depend on it.
+FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, bool rows,
+                         int cus) {
   FusedLayout L{};
   const int64_t P = T * K;
   const bool fp8 = is_fp8(wd);
@@ -122,9 +138,10 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, b
     L.nblk_t = P / bmt + big_experts;
     L.cap_t = L.nblk_t * bmt;
   }
-  L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem, L.bm);
-  L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem, L.bm);
+  L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem, L.bm, cus);
+  L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem, L.bm, cus);
   if (L.tiled) L.dn.splits = 1;          // the tiled products write one part
+  const int dw_parts = L.tiled ? 1 : decode_max_splits(L.nblk, H, (int64_t)I * welem);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   L.ids = take(P * 4);
@@ -142,7 +159,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, b
   L.qx = take(fp8 ? (size_t)T * H : 0);
   L.a = take((size_t)P * I * (fp8 ? 4 : 2));
   L.qa = take(fp8 ? (size_t)P * I : 0);
-  L.dw = take((size_t)L.dn.splits * P * H * (L.tiled ? 2 : 4));   // bfloat16 at prefill
+  L.dw = take((size_t)dw_parts * P * H * (L.tiled ? 2 : 4));   // bfloat16 at prefill
   L.total = off;
   return L;
 }
@@ -267,7 +284,46 @@ size_t moe_fused_workspace_bytes(const moe_fused_args* a) {
   if (is_fp8(a->wdtype) && a->fp8_scales != MOE_SCALES_TENSOR &&
       a->fp8_scales != MOE_SCALES_ROW)
     return 0;
-  return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype, rows_mode(a)).total;
+  return fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype, rows_mode(a), 256).total;
+}
+
+moe_status moe_fused_workspace_layout(const moe_fused_args* a, moe_fused_layout* out) {
+  if (!a || !out) return MOE_ERR_NULL;
+  moe_status st = check_shape(a->T, a->H, a->I, a->E, a->K);
+  if (st != MOE_OK) return st;
+  if (!wdtype_ok(a->wdtype)) return MOE_ERR_UNSUPPORTED;
+  const bool fp8 = is_fp8(a->wdtype);
+  if (fp8 && a->fp8_scales != MOE_SCALES_TENSOR && a->fp8_scales != MOE_SCALES_ROW)
+    return MOE_ERR_UNSUPPORTED;
+  const bool rows = rows_mode(a);
+  const FusedLayout L = fused_layout(a->T, a->H, a->I, a->E, a->K, a->wdtype, rows, 256);
+  const size_t none = MOE_NO_SECTION;
+  moe_fused_layout o{};
+  o.total = L.total;
+  o.block_m = L.bm;
+  o.tiled = L.tiled ? 1 : 0;
+  o.tile_block_m = L.tiled ? tile_block_m() : 0;
+  o.tile_threshold = L.tiled ? kTileThreshold : 0;
+  o.capacity = L.cap;
+  o.tile_capacity = L.tiled ? L.cap_t : 0;
+  o.topk_ids = L.ids;
+  o.topk_weights = L.wts;
+  o.sorted_ids = L.sorted;
+  o.block_expert = L.bexp;
+  o.num_post_pad = L.npp;
+  o.tile_sorted_ids = L.tiled ? L.sorted_t : none;
+  o.tile_block_expert = L.tiled ? L.bexp_t : none;
+  o.tile_num_post_pad = L.tiled ? L.npp_t : none;
+  const bool tensor_fp8 = fp8 && !rows;
+  o.x_amax = tensor_fp8 ? L.scal + (size_t)kAmaxFinal * 4 : none;
+  o.x_codes = fp8 ? L.qx : none;
+  o.x_scales = rows ? L.srow : none;
+  o.a = L.a;
+  o.a_amax = tensor_fp8 ? L.scal + (size_t)(kAmaxWords + kAmaxFinal) * 4 : none;
+  o.a_codes = fp8 ? L.qa : none;
+  o.a_scales = rows ? L.srow + (size_t)a->T * 4 : none;
+  *out = o;
+  return MOE_OK;
 }
 
 }  // extern "C"
@@ -279,27 +335,38 @@ hipError_t mark(hipEvent_t* events, int s, hipStream_t stream) {
   return (events && events[s]) ? hipEventRecord(events[s], stream) : hipSuccess;
 }
 
-moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEvent_t* ev) {
+// Host-only checks of a fused call (no HIP call); the workspace pointer is
+// checked only when `with_workspace`.  T == 0 passes once the shape is valid.
+moe_status check_fused(const moe_fused_args* a, bool with_workspace) {
   if (!a) return MOE_ERR_NULL;
   moe_status st = check_shape(a->T, a->H, a->I, a->E, a->K);
   if (st != MOE_OK) return st;
   if (!wdtype_ok(a->wdtype)) return MOE_ERR_UNSUPPORTED;
   const bool fp8 = is_fp8(a->wdtype);
-  const int fmt = fmt_of(a->wdtype);
   if (fp8 && a->fp8_scales != MOE_SCALES_TENSOR && a->fp8_scales != MOE_SCALES_ROW)
     return MOE_ERR_UNSUPPORTED;
   if (a->T == 0) return MOE_OK;
   const bool rows = rows_mode(a);
-  if (!a->x || !a->router_logits || !a->w13 || !a->w2 || !a->out || !a->workspace)
-    return MOE_ERR_NULL;
+  if (!a->x || !a->router_logits || !a->w13 || !a->w2 || !a->out) return MOE_ERR_NULL;
+  if (with_workspace && !a->workspace) return MOE_ERR_NULL;
   if (fp8 && (!a->w13_scale || !a->w2_scale)) return MOE_ERR_NULL;
   if (rows && (!aligned16(a->w13_scale) || !aligned16(a->w2_scale))) return MOE_ERR_UNSUPPORTED;
-  if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->out) ||
-      !aligned16(a->workspace))
+  if (!aligned16(a->x) || !aligned16(a->w13) || !aligned16(a->w2) || !aligned16(a->out))
     return MOE_ERR_UNSUPPORTED;
+  if (with_workspace && !aligned16(a->workspace)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEvent_t* ev) {
+  moe_status st = check_fused(a, true);
+  if (st != MOE_OK || a->T == 0) return st;
+  const bool fp8 = is_fp8(a->wdtype);
+  const int fmt = fmt_of(a->wdtype);
+  const bool rows = rows_mode(a);
   const int64_t T = a->T;
   const int H = a->H, I = a->I, E = a->E, K = a->K;
-  const FusedLayout L = fused_layout(T, H, I, E, K, a->wdtype, rows);
+  const int cus = num_cus();
+  const FusedLayout L = fused_layout(T, H, I, E, K, a->wdtype, rows, cus);
   if (a->workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
 
@@ -319,7 +386,6 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   uint8_t* qa = ws + L.qa;
   void* dw = ws + L.dw;
   const int P = (int)(T * K);
-  const int cus = num_cus();
   const int welem = fp8 ? 1 : 2;
 
   int32_t* sorted_t = reinterpret_cast<int32_t*>(ws + L.sorted_t);

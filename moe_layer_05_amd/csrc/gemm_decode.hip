@@ -163,9 +163,11 @@ __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
   const int row_bytes = (int)p.row_bytes;
   const int nchunks = (row_bytes + kChunk - 1) / kChunk;
   const int nfull = row_bytes / kChunk;
-  const int cps = (nchunks + p.splits - 1) / p.splits;
-  const int c_begin = split * cps;
-  const int c_end = min(nchunks, c_begin + cps);
+  // Even parts: part s takes chunks [s * n / S, (s + 1) * n / S), so no part is
+  // empty (the host keeps n / S >= 8) and only the last one holds the row's
+  // partial chunk.
+  const int c_begin = (int)((int64_t)split * nchunks / p.splits);
+  const int c_end = (int)((int64_t)(split + 1) * nchunks / p.splits);
 
   // valid tokens of this block (sentinels sit at the end of a block)
   const int32_t* blk = p.sorted_ids + (int64_t)b * p.BM;
@@ -816,11 +818,21 @@ hipError_t prepare_decode_kernels() {
 namespace {
 
 // Waves of one shape that the chip holds at once: one wave per workgroup with
-// D * (RA + NSUB) 4 KB LDS tiles, 160 KB of LDS per compute unit, 256 units.
-int64_t resident_waves(int ra, int nsub, int64_t row_bytes) {
+// D * (RA + NSUB) 4 KB LDS tiles, 160 KB of LDS per compute unit.
+int64_t resident_waves(int ra, int nsub, int64_t row_bytes, int num_cus) {
   const int d = row_bytes <= kChunk ? 1 : ring_depth(ra, nsub);
   const int per_cu = (160 * 1024) / (d * (ra + nsub) * kTileBytes);
-  return 256LL * (per_cu > 0 ? per_cu : 1);
+  return (int64_t)std::max(num_cus, 1) * (per_cu > 0 ? per_cu : 1);
+}
+
+// Parts of the down product's reduction for RA weight tiles per wave: split
+// while there are too few waves to cover the chip (about 2048 in flight),
+// keeping >= 8 chunks per part.
+int down_splits(int64_t nblk_cap, int rows, int nchunks, int ra) {
+  const int64_t units = nblk_cap * ((rows + 16 * ra - 1) / (16 * ra));
+  int sp = 1;
+  while (units * sp < 2048 && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
+  return sp;
 }
 
 // Busy fraction of the rounds a grid of `units` waves takes (the last round
@@ -832,7 +844,8 @@ double round_fill(int64_t units, int64_t resident) {
 
 }  // namespace
 
-DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm) {
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm,
+                         int num_cus) {
   DecodeShape s{};
   const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
   const int nsub = bm / 16;
@@ -843,8 +856,8 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
   auto pick = [&](int pref, auto units_of) {
     if (nchunks < 24) return 2;
     const int alt = 6 - pref;
-    const double fp = round_fill(units_of(pref), resident_waves(pref, nsub, row_bytes));
-    const double fa = round_fill(units_of(alt), resident_waves(alt, nsub, row_bytes));
+    const double fp = round_fill(units_of(pref), resident_waves(pref, nsub, row_bytes, num_cus));
+    const double fa = round_fill(units_of(alt), resident_waves(alt, nsub, row_bytes, num_cus));
     return fa > fp + 0.05 ? alt : pref;
   };
   if (mode == kGateUp) {
@@ -856,15 +869,9 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
     s.groups = (rows + 8 * s.ra - 1) / (8 * s.ra);
     s.splits = 1;
   } else {
-    // rows = H: RA 16-row tiles per wave; short rows take more tiles.  Split
-    // the reduction when there are too few waves to cover the chip (about
-    // 2048 in flight), keeping >= 8 chunks per part.
-    auto splits_of = [&](int ra) {
-      const int64_t units = nblk_cap * ((rows + 16 * ra - 1) / (16 * ra));
-      int sp = 1;
-      while (units * sp < 2048 && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
-      return sp;
-    };
+    // rows = H: RA 16-row tiles per wave; short rows take more tiles; the
+    // reduction is split as down_splits says.
+    auto splits_of = [&](int ra) { return down_splits(nblk_cap, rows, nchunks, ra); };
     auto units = [&](int ra) {
       return nblk_cap * ((rows + 16 * ra - 1) / (16 * ra)) * splits_of(ra);
     };
@@ -877,6 +884,13 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
     s.splits = splits_of(s.ra);
   }
   return s;
+}
+
+int decode_max_splits(int64_t nblk_cap, int rows, int64_t row_bytes) {
+  const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
+  int m = 1;
+  for (int ra : {2, 4, 8}) m = std::max(m, down_splits(nblk_cap, rows, nchunks, ra));
+  return m;
 }
 
 hipError_t launch_gemm_decode(int mode, int fmt, const GemmParams& p, int ra, int64_t nblk_cap,

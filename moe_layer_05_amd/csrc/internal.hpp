@@ -115,7 +115,13 @@ hipError_t prepare_front_kernels();
 hipError_t prepare_quant_kernels();
 hipError_t prepare_combine_kernels();
 
-DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm);
+
+// The shape is chosen for num_cus compute units (the current device's).
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm,
+                         int num_cus);
+// The most parts any shape choice splits the down product's reduction into,
+// whatever the device (bounds the workspace of the partial rows).
+int decode_max_splits(int64_t nblk_cap, int rows, int64_t row_bytes);
 hipError_t launch_gemm_decode(int mode, int fmt, const GemmParams& p, int ra, int64_t nblk_cap,
                               int num_cus, hipStream_t stream);
 

@@ -73,6 +73,31 @@ int main(void) {
     assert vals == want
 
 
+def test_layout_struct_matches_c():
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    F = binding.FusedLayout
+    names = [n for n, _ in F._fields_]
+    prog = ('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
+            'int main(void) {\n  printf("%zu %zu", sizeof(moe_fused_layout), (size_t)MOE_NO_SECTION);\n'
+            + "".join(f'  printf(" %zu", offsetof(moe_fused_layout, {n}));\n' for n in names)
+            + "  return 0;\n}\n")
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "l.c")
+        open(c, "w").write(prog)
+        exe = os.path.join(d, "l")
+        r = subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                            f"-I{os.path.join(ROOT, 'include')}", c, "-o", exe],
+                           capture_output=True, text=True)
+        if r.returncode:
+            pytest.skip("cannot compile against hip_runtime_api.h: " + r.stderr[:200])
+        vals = [int(v) for v in subprocess.check_output([exe], text=True).split()]
+    want = [ctypes.sizeof(F), binding.NO_SECTION] + [getattr(F, n).offset for n in names]
+    assert vals == want
+
+
 def test_status_strings(L):
     for s in range(6):
         assert L.moe_status_string(s).decode().startswith(binding.STATUS[s])
@@ -186,3 +211,104 @@ def test_fused_block_m_and_workspace(L):
     a.fp8_scales = 0
     a.K = 99
     assert L.moe_fused_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def _layout(L, **kw):
+    a = _args(**kw)
+    out = binding.FusedLayout()
+    st = L.moe_fused_workspace_layout(ctypes.byref(a), ctypes.byref(out))
+    return st, out
+
+
+def _sections(lay):
+    return {n: getattr(lay, n) for n in ("topk_ids", "topk_weights", "sorted_ids",
+                                         "block_expert", "num_post_pad", "tile_sorted_ids",
+                                         "tile_block_expert", "tile_num_post_pad", "x_amax",
+                                         "x_codes", "x_scales", "a", "a_amax", "a_codes",
+                                         "a_scales")}
+
+
+def test_workspace_layout_query(L):
+    """The layout query agrees with the size query and with the block size,
+    marks the sections a call does not have, and its sections lie inside the
+    workspace without overlapping (sizes from the documented shapes)."""
+    NO = binding.NO_SECTION
+    assert L.moe_fused_workspace_layout(None, None) == NULL
+    assert _layout(L, K=17)[0] == SHAPE
+    for kw in (dict(), dict(fp8_scales=1), dict(wdtype=0), dict(wdtype=2),
+               dict(T=4096, H=7168, I=2048, E=256, K=8),
+               dict(T=4096, H=7168, I=2048, E=256, K=8, wdtype=0),
+               dict(T=1, H=4096, I=14336, E=8, K=2, wdtype=0)):
+        st, lay = _layout(L, **kw)
+        assert st == OK, kw
+        a = _args(**kw)
+        assert lay.total == L.moe_fused_workspace_bytes(ctypes.byref(a))
+        assert lay.block_m == L.moe_fused_block_m(a.T, a.H, a.I, a.E, a.K, a.wdtype) or lay.tiled
+        fp8 = a.wdtype != 0
+        rows = fp8 and a.fp8_scales == 1
+        sec = _sections(lay)
+        assert (sec["x_codes"] != NO) == fp8 and (sec["a_codes"] != NO) == fp8
+        assert (sec["x_amax"] != NO) == (fp8 and not rows)
+        assert (sec["a_amax"] != NO) == (fp8 and not rows)
+        assert (sec["x_scales"] != NO) == rows and (sec["a_scales"] != NO) == rows
+        assert (sec["tile_sorted_ids"] != NO) == bool(lay.tiled)
+        P = a.T * a.K
+        size = {"topk_ids": 4 * P, "topk_weights": 4 * P, "sorted_ids": 4 * lay.capacity,
+                "block_expert": 4 * lay.capacity // lay.block_m, "num_post_pad": 4,
+                "tile_sorted_ids": 4 * lay.tile_capacity,
+                "tile_block_expert": 4 * lay.tile_capacity // max(lay.tile_block_m, 1),
+                "tile_num_post_pad": 4, "x_amax": 4, "x_codes": a.T * a.H,
+                "x_scales": 4 * a.T, "a": P * a.I * (4 if fp8 else 2), "a_amax": 4,
+                "a_codes": P * a.I, "a_scales": 4 * P}
+        spans = sorted((off, off + size[n], n) for n, off in sec.items() if off != NO)
+        for (o0, e0, n0), (o1, _, n1) in zip(spans, spans[1:]):
+            assert e0 <= o1, (n0, n1)
+        assert spans[-1][1] <= lay.total
+        if lay.tiled:
+            assert lay.tile_block_m == 256 and lay.tile_threshold == 16 and lay.block_m == 16
+
+
+def test_workspace_bytes_bound_the_down_parts(L):
+    """The partial-row buffer is sized for the most parts any shape choice
+    could split the down product into, so the size does not depend on the
+    device: a one-token call whose I spans 129 chunks (16 parts)."""
+    a = _args(T=1, H=256, I=16400, E=2, K=1, wdtype=0)
+    n = L.moe_fused_workspace_bytes(ctypes.byref(a))
+    assert n >= 16 * 1 * 256 * 4
+
+
+class _Buf:
+    def __init__(self, n):
+        self.n = n
+
+    def numel(self):
+        return self.n
+
+
+def test_workspace_pool_policy():
+    """Per-stream workspaces: reused per key, grown when too small, at most
+    max_entries kept (least recently used dropped), release drops them."""
+    made = []
+
+    def alloc(n, key, ctx):
+        made.append((key, n, ctx))
+        return _Buf(n)
+
+    pool = binding.WorkspacePool(alloc, max_entries=2)
+    a = pool.get("s1", 1000, "ctx1")
+    assert a.numel() == 1000 and made[-1] == ("s1", 1000, "ctx1")
+    assert pool.get("s1", 500) is a and len(made) == 1          # reused: large enough
+    b = pool.get("s1", 4000)
+    assert b is not a and b.numel() == 4000 and len(pool) == 1  # grown in place of a
+    pool.get("s2", 10)
+    assert pool.get("s2", 10).numel() == 256                    # minimum size
+    pool.get("s1", 10)                                          # s1 most recent now
+    pool.get("s3", 10)                                          # evicts s2
+    assert pool.keys() == ["s1", "s3"] and len(pool) == 2
+    pool.release("s1")
+    assert pool.keys() == ["s3"]
+    pool.release()
+    assert len(pool) == 0
+    with pytest.raises(ValueError):
+        binding.WorkspacePool(alloc, max_entries=0)
+
