@@ -311,6 +311,44 @@ typedef enum {
 moe_status moe_fused_forward_timed(const moe_fused_args* args, hipStream_t stream,
                                    hipEvent_t* events);
 
+/*
+ * Inverse rotary position embedding of attention heads fused with one FP8
+ * scale per (token, head): the attention-side kernel the pages name beside
+ * the MoE layer, which must serve any number of tokens without compiling
+ * anything for a new count (toolboxkart.tech page, section 3; aib.vote page,
+ * fourth paragraph: a kernel recompiled per num_tokens until its
+ * variable-length arguments were left unspecialised).  Here T, NH, D and R
+ * are plain arguments of one precompiled kernel.
+ *
+ * For token t at position p = positions[t] and each head h, with the pairs
+ * (i, i + R/2) (interleaved == 0) or (2i, 2i + 1) (interleaved != 0),
+ * i < R/2, c = cos_sin[p][i] and s = cos_sin[p][R/2 + i]:
+ *   y1 = x1 * c + x2 * s,   y2 = x2 * c - x1 * s      (rotation by -theta)
+ * in float32, each product and sum rounded on its own; features R..D-1 pass
+ * through.  Then scales[t][h] = amax|y| / max of fmt (448 for E4M3, 57344
+ * for E5M2; 1 when the row is zero) and codes[t][h][:] = FP8(y / scale) with
+ * an IEEE float32 division, nearest even, saturating (as moe_act_quant_fp8).
+ *
+ *   x          [T][NH][D] bfloat16; token t starts at element
+ *              t * x_token_stride (heads contiguous inside a token), 16-byte
+ *              aligned
+ *   positions  [T] int64; a position outside [0, max_pos) is clamped into it
+ *   cos_sin    [max_pos][R] float32: the R/2 cosines, then the R/2 sines, of
+ *              each position's angles; 16-byte aligned
+ *   codes      [T][NH][D] uint8 (out), 16-byte aligned
+ *   scales     [T][NH] float32 (out)
+ * Supported: D % 8 == 0 and D <= 512; R even, 0 < R <= D, R % 16 == 0
+ * (R % 8 == 0 when interleaved); x_token_stride >= NH * D and a multiple of
+ * 8; fmt MOE_FP8_E4M3 or MOE_FP8_E5M2.  Errors: MOE_ERR_SHAPE,
+ * MOE_ERR_UNSUPPORTED, MOE_ERR_NULL (host checks, nothing enqueued),
+ * MOE_ERR_HIP when the launch fails.  T == 0 enqueues nothing.
+ */
+moe_status moe_inv_rope_fp8_quant_per_head(const void* x, int64_t x_token_stride,
+                                           const int64_t* positions, const float* cos_sin,
+                                           int64_t max_pos, int64_t T, int32_t NH, int32_t D,
+                                           int32_t R, int32_t interleaved, moe_wdtype fmt,
+                                           uint8_t* codes, float* scales, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -117,6 +117,10 @@ _SIGS = {
     "moe_fused_forward": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p]),
     "moe_fused_forward_timed": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p,
                                                ctypes.c_void_p]),
+    "moe_inv_rope_fp8_quant_per_head": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 # Stage boundaries of moe_fused_forward_timed (moe_stage in include/moe.h).
@@ -231,6 +235,43 @@ def act_quant_fp8_rows(x, fmt="e4m3", stream=None):
     _check(lib().moe_act_quant_fp8_rows(xp, x.shape[0], x.shape[1], _FP8_WDTYPE[fmt],
                                         _ptr(codes), _ptr(scales), _stream(stream)),
            "moe_act_quant_fp8_rows")
+    return codes, scales
+
+
+# ------------------------------------------------------------------ attention side
+
+def inv_rope_fp8_quant_per_head(x, positions, cos_sin, R, interleaved=False, fmt="e4m3",
+                                codes=None, scales=None, stream=None):
+    """(codes uint8 [T, NH, D], scales float32 [T, NH]): the inverse rotary
+    embedding of bfloat16 heads x [T, NH, D] (token rows may be strided, the
+    heads of a token contiguous) at int64 ``positions`` [T] with the float32
+    table ``cos_sin`` [max_pos, R], then one FP8 scale per (token, head)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [T, NH, D]")
+    T, NH, D = x.shape
+    if not x.is_cuda or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a bfloat16 CUDA (HIP) tensor")
+    if x.stride(2) != 1 or x.stride(1) != D:
+        raise ValueError("the heads of a token must be contiguous")
+    pp = _dev(positions, torch.int64, "positions")
+    cp = _dev(cos_sin, torch.float32, "cos_sin")
+    if tuple(positions.shape) != (T,):
+        raise ValueError(f"positions must be [{T}]")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != R:
+        raise ValueError(f"cos_sin must be [max_pos, {R}]")
+    if codes is None:
+        codes = torch.empty(T, NH, D, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(T, NH, dtype=torch.float32, device=x.device)
+    _dev(codes, torch.uint8, "codes")
+    _dev(scales, torch.float32, "scales")
+    if tuple(codes.shape) != (T, NH, D) or tuple(scales.shape) != (T, NH):
+        raise ValueError("codes must be [T, NH, D] and scales [T, NH]")
+    stride = x.stride(0) if T > 1 else NH * D
+    _check(lib().moe_inv_rope_fp8_quant_per_head(
+        ctypes.c_void_p(x.data_ptr()), stride, pp, cp, cos_sin.shape[0], T, NH, D, R,
+        int(bool(interleaved)), _FP8_WDTYPE[fmt], _ptr(codes), _ptr(scales), _stream(stream)),
+        "moe_inv_rope_fp8_quant_per_head")
     return codes, scales
 
 

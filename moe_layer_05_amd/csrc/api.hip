@@ -50,6 +50,7 @@ hipError_t prepare_all() {
   if (e == hipSuccess) e = prepare_front_kernels();
   if (e == hipSuccess) e = prepare_quant_kernels();
   if (e == hipSuccess) e = prepare_combine_kernels();
+  if (e == hipSuccess) e = prepare_rope_kernels();
   if (e == hipSuccess) st.prepared = true;
   return e;
 }
@@ -526,6 +527,27 @@ moe_status moe_fused_forward_timed(const moe_fused_args* a, hipStream_t stream,
                                    hipEvent_t* events) {
   if (!events) return MOE_ERR_NULL;
   return fused_forward_impl(a, stream, events);
+}
+
+moe_status moe_inv_rope_fp8_quant_per_head(const void* x, int64_t x_token_stride,
+                                           const int64_t* positions, const float* cos_sin,
+                                           int64_t max_pos, int64_t T, int32_t NH, int32_t D,
+                                           int32_t R, int32_t interleaved, moe_wdtype fmt,
+                                           uint8_t* codes, float* scales, hipStream_t stream) {
+  if (T < 0 || NH <= 0 || D <= 0 || R <= 0 || max_pos <= 0) return MOE_ERR_SHAPE;
+  if (R > D || (R & 1)) return MOE_ERR_SHAPE;
+  if (!is_fp8(fmt)) return MOE_ERR_UNSUPPORTED;
+  if (D % 8 != 0 || D > 512) return MOE_ERR_UNSUPPORTED;
+  if (interleaved ? (R % 8 != 0) : (R % 16 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (x_token_stride < (int64_t)NH * D || x_token_stride % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)NH >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !positions || !cos_sin || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(cos_sin)) return MOE_ERR_UNSUPPORTED;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_inv_rope_quant(fmt_of(fmt), interleaved != 0, x, x_token_stride,
+                                          positions, cos_sin, max_pos, T, NH, D, R, codes,
+                                          scales, num_cus(), stream));
 }
 
 }  // extern "C"

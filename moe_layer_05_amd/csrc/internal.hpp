@@ -114,7 +114,15 @@ hipError_t prepare_align_kernels();
 hipError_t prepare_front_kernels();
 hipError_t prepare_quant_kernels();
 hipError_t prepare_combine_kernels();
+hipError_t prepare_rope_kernels();
 
+// Inverse rotary embedding of [T][NH][D] bfloat16 heads (token stride x_stride
+// elements) with the cos/sin table [max_pos][R], then one FP8 scale per
+// (token, head): codes [T][NH][D], scales [T][NH].
+hipError_t launch_inv_rope_quant(int fmt, bool interleaved, const void* x, int64_t x_stride,
+                                 const int64_t* positions, const float* table, int64_t max_pos,
+                                 int64_t T, int NH, int D, int R, uint8_t* codes, float* scales,
+                                 int num_cus, hipStream_t stream);
 
 // The shape is chosen for num_cus compute units (the current device's).
 DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm,

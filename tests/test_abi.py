@@ -312,3 +312,20 @@ def test_workspace_pool_policy():
     with pytest.raises(ValueError):
         binding.WorkspacePool(alloc, max_entries=0)
 
+
+def test_inv_rope_validation(L):
+    p = ctypes.c_void_p(256)
+    E4, E5 = binding.MOE_FP8_E4M3, binding.MOE_FP8_E5M2
+    f = L.moe_inv_rope_fp8_quant_per_head
+    assert f(p, 512, p, p, 100, 4, 4, 128, 130, 0, E4, p, p, None) == SHAPE     # R > D
+    assert f(p, 512, p, p, 100, 4, 4, 128, 63, 0, E4, p, p, None) == SHAPE      # odd R
+    assert f(p, 512, p, p, 100, 4, 4, 128, 24, 0, E4, p, p, None) == UNSUP      # half: R % 16
+    assert f(p, 512, p, p, 100, 4, 4, 128, 20, 1, E5, p, p, None) == UNSUP      # R % 8
+    assert f(p, 4 * 520, p, p, 100, 4, 4, 520, 16, 0, E4, p, p, None) == UNSUP  # D > 512
+    assert f(p, 512, p, p, 100, 4, 4, 124, 16, 0, E4, p, p, None) == UNSUP     # D % 8
+    assert f(p, 256, p, p, 100, 4, 4, 128, 128, 0, E4, p, p, None) == UNSUP    # stride < NH*D
+    assert f(p, 512, p, p, 100, 4, 4, 128, 128, 0, binding.MOE_BF16, p, p, None) == UNSUP
+    assert f(p, 512, None, p, 100, 4, 4, 128, 128, 0, E4, p, p, None) == NULL
+    assert f(ctypes.c_void_p(258), 512, p, p, 100, 4, 4, 128, 128, 0, E4, p, p, None) == UNSUP
+    assert f(p, 512, p, p, 0, 4, 4, 128, 128, 0, E4, p, p, None) == SHAPE       # empty table
+    assert f(None, 512, None, None, 100, 0, 4, 128, 128, 0, E4, None, None, None) == OK
