@@ -349,6 +349,28 @@ moe_status moe_inv_rope_fp8_quant_per_head(const void* x, int64_t x_token_stride
                                            int32_t R, int32_t interleaved, moe_wdtype fmt,
                                            uint8_t* codes, float* scales, hipStream_t stream);
 
+/*
+ * moe_fused_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same layer and the same kernels, with the workspace taken
+ * from a scratch buffer the library holds in device memory instead of from
+ * args->workspace (args->workspace and args->workspace_bytes are ignored).
+ * Nothing is allocated: the buffer is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES, one copy per GPU the library runs on, held until
+ * the process ends.  The first call on a device resolves the kernels and the
+ * buffer's address there (no allocation).  Every call on a GPU uses that
+ * GPU's one buffer and leaves the last call's contents in it (each call sets
+ * up what it reads, so the contents on entry do not matter); calls whose
+ * execution overlaps on one GPU (on different streams, or from different
+ * threads without ordering) race on it and give undefined results.
+ * Errors: as moe_fused_forward, and MOE_ERR_WORKSPACE, before anything is
+ * enqueued, when moe_fused_workspace_bytes(args) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (decode batches fit; a 4096-token call of a
+ * 256-expert layer does not).
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_fused_forward_noalloc(const moe_fused_args* args, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

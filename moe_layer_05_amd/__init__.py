@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     align_capacity,
     fused_block_m,
     fused_forward,
+    fused_forward_noalloc,
     inv_rope_fp8_quant_per_head,
     lib,
     route_topk,

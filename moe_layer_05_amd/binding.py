@@ -117,6 +117,7 @@ _SIGS = {
     "moe_fused_forward": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p]),
     "moe_fused_forward_timed": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p,
                                                ctypes.c_void_p]),
+    "moe_fused_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(FusedArgs), ctypes.c_void_p]),
     "moe_inv_rope_fp8_quant_per_head": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -463,6 +464,19 @@ class FusedMoE:
             _check(lib().moe_fused_forward_timed(ctypes.byref(a), _stream(stream), arr),
                    "moe_fused_forward_timed")
         return (out, ids, wts) if return_topk else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20           # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def fused_forward_noalloc(layer, x, logits, out, ids=None, wts=None, stream=None):
+    """moe_fused_forward_noalloc: the layer ``layer`` (a FusedMoE) on x and
+    logits into the caller's ``out`` (and optional ids / wts), with the
+    library's own scratch buffer as workspace; nothing is allocated."""
+    a = layer.args(x, logits, out, ids, wts)
+    _check(lib().moe_fused_forward_noalloc(ctypes.byref(a), _stream(stream)),
+           "moe_fused_forward_noalloc")
+    return out
 
 
 def fused_forward(x, logits, w13, w2, K, w13_scale=None, w2_scale=None, renormalize=True,

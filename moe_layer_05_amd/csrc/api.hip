@@ -25,6 +25,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct DeviceState {
   bool prepared = false;
   int cus = 0;
+  void* scratch = nullptr;        // this device's copy of `scratch` (device address)
 };
 std::mutex g_dev_mu;
 std::vector<DeviceState> g_dev;   // indexed by device id; guarded by g_dev_mu
@@ -34,7 +35,15 @@ DeviceState& device_state(int dev) {
   return g_dev[(size_t)dev];
 }
 
-// Resolves every kernel on the current device once; returns the first error.
+// Workspace of moe_fused_forward_noalloc: one copy per device, held until the
+// process ends.  In host code this name is a stand-in, not a device address;
+// the address of the current device's copy comes from hipGetSymbolAddress
+// (kept in DeviceState::scratch) and is the only form host code passes on.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Resolves every kernel on the current device once, and the address of its
+// scratch copy; returns the first error.
 hipError_t prepare_all() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -51,8 +60,19 @@ hipError_t prepare_all() {
   if (e == hipSuccess) e = prepare_quant_kernels();
   if (e == hipSuccess) e = prepare_combine_kernels();
   if (e == hipSuccess) e = prepare_rope_kernels();
+  if (e == hipSuccess) e = hipGetSymbolAddress(&st.scratch, HIP_SYMBOL(scratch));
+  if (e == hipSuccess && st.scratch == nullptr) e = hipErrorInvalidSymbol;
   if (e == hipSuccess) st.prepared = true;
   return e;
+}
+
+// The current device's scratch address (prepare_all has run on it), or null.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  const DeviceState& st = device_state(dev);
+  return st.prepared ? st.scratch : nullptr;
 }
 
 // Compute-unit count of the current device (256, MI355X's, when no device
@@ -548,6 +568,20 @@ moe_status moe_inv_rope_fp8_quant_per_head(const void* x, int64_t x_token_stride
   return hip_status(launch_inv_rope_quant(fmt_of(fmt), interleaved != 0, x, x_token_stride,
                                           positions, cos_sin, max_pos, T, NH, D, R, codes,
                                           scales, num_cus(), stream));
+}
+
+moe_status moe_fused_forward_noalloc(const moe_fused_args* a, hipStream_t stream) {
+  // every check on the host first: arguments, then the size against the
+  // scratch buffer; nothing is enqueued on an error
+  const moe_status st = check_fused(a, false);
+  if (st != MOE_OK || a->T == 0) return st;
+  if (moe_fused_workspace_bytes(a) > kScratchBytes) return MOE_ERR_WORKSPACE;
+  if (prepare_all() != hipSuccess) return MOE_ERR_HIP;
+  moe_fused_args b = *a;
+  b.workspace = device_scratch();
+  if (!b.workspace) return MOE_ERR_HIP;
+  b.workspace_bytes = kScratchBytes;
+  return fused_forward_impl(&b, stream, nullptr);
 }
 
 }  // extern "C"

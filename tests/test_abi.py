@@ -313,6 +313,20 @@ def test_workspace_pool_policy():
         binding.WorkspacePool(alloc, max_entries=0)
 
 
+def test_noalloc_validation(L):
+    """The no-allocation entry point checks everything on the host first: a
+    call whose workspace exceeds the scratch buffer is refused, as are bad
+    arguments, without touching a device (none is present here)."""
+    big = _args(T=4096, H=7168, I=2048, E=256, K=8, workspace=None, workspace_bytes=0)
+    assert L.moe_fused_workspace_bytes(ctypes.byref(big)) > binding.NOALLOC_SCRATCH_BYTES
+    assert L.moe_fused_forward_noalloc(ctypes.byref(big), None) == WS
+    assert L.moe_fused_forward_noalloc(None, None) == NULL
+    assert L.moe_fused_forward_noalloc(ctypes.byref(_args(K=17)), None) == SHAPE
+    assert L.moe_fused_forward_noalloc(ctypes.byref(_args(x=None)), None) == NULL
+    assert L.moe_fused_forward_noalloc(ctypes.byref(_args(out=4097)), None) == UNSUP
+    assert L.moe_fused_forward_noalloc(ctypes.byref(_args(T=0, x=None, out=None)), None) == OK
+
+
 def test_inv_rope_validation(L):
     p = ctypes.c_void_p(256)
     E4, E5 = binding.MOE_FP8_E4M3, binding.MOE_FP8_E5M2
