@@ -1,4 +1,6 @@
 // a2: align kernel -- one workgroup runs align_block (align_device.hpp).
+#include <algorithm>
+
 #include "align_device.hpp"
 #include "internal.hpp"
 
@@ -9,6 +11,71 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int P, int E, AlignOut out, int32_t* __restrict__ rank) {
   extern __shared__ int smem[];
   align_block(ids, P, E, out, rank, smem);
+}
+
+// Align plus a0 in one launch (small batches routed by the router kernel):
+// workgroup 0 runs align_block; workgroups 1.. write the FP8 codes of x, with
+// one scale per tensor (the router launch left the amax of x in the slots of
+// amax_x: each workgroup folds them, workgroup 1 stores the final word) or one
+// scale per token row (a wave per row, as quant_rows_kernel).  The codes are
+// formed with the same arithmetic as the quantisation kernels.
+struct XQuant {
+  const uint4* x;            // [T][H] bfloat16, 8 per uint4
+  int64_t n8;                // T * H / 8
+  int h8;                    // H / 8
+  uint32_t* amax_x;          // per tensor: amax block of x (slots in, final word out)
+  uint2* codes;              // 8 codes per uint2
+  float* row_scales;         // per row: [T] scales out, or nullptr for one scale
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kAlignThreads) void align_quant_kernel(
+    const int32_t* __restrict__ ids, int P, int E, AlignOut out, int32_t* __restrict__ rank,
+    XQuant q) {
+  extern __shared__ int smem[];
+  if (blockIdx.x == 0) {
+    align_block(ids, P, E, out, rank, smem);
+    return;
+  }
+  const int nq = gridDim.x - 1, b = blockIdx.x - 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (q.row_scales) {
+    const int64_t T = q.n8 / q.h8;
+    for (int64_t r = (int64_t)b * kAlignWaves + threadIdx.x / kWave; r < T;
+         r += (int64_t)nq * kAlignWaves) {
+      const uint4* row = q.x + r * q.h8;
+      float m = 0.0f;
+      for (int j = lane; j < q.h8; j += kWave) {
+        const uint4 v = row[j];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))),
+                           fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))),
+                           fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+      }
+      m = wave_max_dpp(m);
+      const float sc = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
+      if (lane == 0) q.row_scales[r] = sc;
+      for (int j = lane; j < q.h8; j += kWave) {
+        const uint4 v = row[j];
+        uint2 o;
+        o.x = fp8_pack4<FMT>(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), sc);
+        o.y = fp8_pack4<FMT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), sc);
+        q.codes[r * q.h8 + j] = o;
+      }
+    }
+    return;
+  }
+  const float m = amax_slots_reduce(q.amax_x);
+  const float sc = scale_from_amax_bits(__float_as_uint(m), fp8_max<FMT>());
+  if (b == 0 && threadIdx.x == 0) q.amax_x[kAmaxFinal] = __float_as_uint(m);
+  for (int64_t j = (int64_t)b * kAlignThreads + threadIdx.x; j < q.n8;
+       j += (int64_t)nq * kAlignThreads) {
+    const uint4 v = q.x[j];
+    uint2 o;
+    o.x = fp8_pack4<FMT>(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), sc);
+    o.y = fp8_pack4<FMT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), sc);
+    q.codes[j] = o;
+  }
 }
 
 // ---- Multi-workgroup form, for many pairs.  (1) Each workgroup ranks the
@@ -118,6 +185,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
 
 hipError_t prepare_align_kernels() {
   const void* fns[] = {reinterpret_cast<const void*>(&align_kernel),
+                       reinterpret_cast<const void*>(&align_quant_kernel<kFmtE4M3>),
+                       reinterpret_cast<const void*>(&align_quant_kernel<kFmtE5M2>),
                        reinterpret_cast<const void*>(&align_count_kernel),
                        reinterpret_cast<const void*>(&align_scan_kernel),
                        reinterpret_cast<const void*>(&align_scatter_kernel)};
@@ -162,6 +231,27 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
                         hipStream_t stream) {
   AlignOut out{sorted_ids, block_expert, num_post_pad, BM};
   align_kernel<<<1, kAlignThreads, align_lds_bytes(E), stream>>>(ids, P, E, out, rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_align_quant(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
+                              int fmt, const void* x, int64_t T, int H, uint32_t* amax_x,
+                              uint8_t* codes, float* row_scales, int num_cus,
+                              hipStream_t stream) {
+  AlignOut out{sorted_ids, block_expert, num_post_pad, BM};
+  XQuant q{static_cast<const uint4*>(x), T * (int64_t)H / 8, H / 8, amax_x,
+           reinterpret_cast<uint2*>(codes), row_scales};
+  int64_t nq = row_scales ? (T + kAlignWaves - 1) / kAlignWaves
+                          : (q.n8 + kAlignThreads - 1) / kAlignThreads;
+  nq = std::max<int64_t>(1, std::min<int64_t>(nq, num_cus));
+  const dim3 grid((unsigned)(1 + nq));
+  if (fmt == kFmtE5M2)
+    align_quant_kernel<kFmtE5M2><<<grid, kAlignThreads, align_lds_bytes(E), stream>>>(
+        ids, P, E, out, rank, q);
+  else
+    align_quant_kernel<kFmtE4M3><<<grid, kAlignThreads, align_lds_bytes(E), stream>>>(
+        ids, P, E, out, rank, q);
   return hipGetLastError();
 }
 

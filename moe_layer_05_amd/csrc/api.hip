@@ -436,23 +436,30 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
         e = launch_router(a->router_logits, T, E, K, a->renormalize, ids, wts, amax_x,
                           tensor_fp8 ? 2 : 0, stream);
     }
-    // a0
+    // a0.  Without tiles (decode batches) the align launch also writes the
+    // codes of x -- from the router's amax slots, or per token row -- so the
+    // act-quant stage is empty; a large x has its amax reduced first by a
+    // launch of its own.
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ACT_QUANT, stream);
-    if (e == hipSuccess && rows) {
-      e = launch_quant_rows(fmt, a->x, true, T, H, qx, sx, cus, stream);
-    } else if (fp8) {
-      if (e == hipSuccess && !amax_in_router)
-        e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
-      if (e == hipSuccess)
-        e = launch_quant_bf16(fmt, a->x, T * H, amax_x, qx, nullptr, cus, stream);
+    const bool quant_in_align = fp8 && !L.tiled;
+    if (fp8 && !rows && !amax_in_router && e == hipSuccess)
+      e = launch_amax_bf16(a->x, T * H, amax_x, cus, stream);
+    if (fp8 && L.tiled && e == hipSuccess) {
+      e = rows ? launch_quant_rows(fmt, a->x, true, T, H, qx, sx, cus, stream)
+               : launch_quant_bf16(fmt, a->x, T * H, amax_x, qx, nullptr, cus, stream);
     }
     // a2
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_ALIGN, stream);
     if (e == hipSuccess) {
-      e = L.tiled ? launch_align_split_multi(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
-                                             sorted_t, bexp_t, npp_t, kTileThreshold, rank,
-                                             reinterpret_cast<int32_t*>(ws + L.ascr), stream)
-                  : launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
+      if (L.tiled)
+        e = launch_align_split_multi(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
+                                     sorted_t, bexp_t, npp_t, kTileThreshold, rank,
+                                     reinterpret_cast<int32_t*>(ws + L.ascr), stream);
+      else if (quant_in_align)
+        e = launch_align_quant(ids, P, E, L.bm, sorted, bexp, npp, rank, fmt, a->x, T, H, amax_x,
+                               qx, rows ? sx : nullptr, cus, stream);
+      else
+        e = launch_align(ids, P, E, L.bm, sorted, bexp, npp, rank, stream);
     }
   }
 

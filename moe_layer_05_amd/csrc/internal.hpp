@@ -62,6 +62,16 @@ hipError_t launch_align(const int32_t* ids, int P, int E, int BM, int32_t* sorte
                         int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
                         hipStream_t stream);
 
+// a2 and a0 in one launch: workgroup 0 aligns, the others write the FP8 codes
+// of x [T][H] (fmt E4M3 or E5M2) with one scale per tensor, from the amax
+// slots of amax_x (final word stored), or, with row_scales set, one scale per
+// token row (written to row_scales).
+hipError_t launch_align_quant(const int32_t* ids, int P, int E, int BM, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* num_post_pad, int32_t* rank,
+                              int fmt, const void* x, int64_t T, int H, uint32_t* amax_x,
+                              uint8_t* codes, float* row_scales, int num_cus,
+                              hipStream_t stream);
+
 // a1 + a0 + a2 by one workgroup for small batches (front_fits): routing,
 // (FP8) the codes of x with the final amax word and the amax slots of a
 // cleared -- or, when sx_rows is set, the codes of x with one scale per token
