@@ -110,7 +110,7 @@ def load_traffic(workload, T, kernel, scales="tensor", fmt="e4m3"):
 
 
 STAGE_KERNELS = {"gate_up": re.compile(r"moe_gemm_\w+_kernel<0,"),
-                 "down": re.compile(r"moe_gemm_\w+_kernel<1,")}
+                 "down": re.compile(r"moe_gemm_\w+_kernel<1,|moe_down_small_kernel")}
 
 
 def read_counter(folder, counter):

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libmoemi.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "router.hip", "align.hip", "front.hip", "quant.hip", "gemm_decode.hip", "gemm_tile.hip",
-           "combine.hip", "rope.hip"]
+           "down_small.hip", "combine.hip", "rope.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

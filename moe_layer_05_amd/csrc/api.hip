@@ -58,6 +58,7 @@ hipError_t prepare_all() {
   if (e == hipSuccess) e = prepare_align_kernels();
   if (e == hipSuccess) e = prepare_front_kernels();
   if (e == hipSuccess) e = prepare_quant_kernels();
+  if (e == hipSuccess) e = prepare_down_small_kernels();
   if (e == hipSuccess) e = prepare_combine_kernels();
   if (e == hipSuccess) e = prepare_rope_kernels();
   if (e == hipSuccess) e = hipGetSymbolAddress(&st.scratch, HIP_SYMBOL(scratch));
@@ -506,6 +507,19 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   else if (e == hipSuccess && fp8)
     e = launch_quant_f32(fmt, static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus,
                          stream);
+  // At most 16 pairs: the down product and the combine in one launch.
+  const SmallDownPlan small = L.tiled ? SmallDownPlan{} : small_down_plan(P, K, H, I, welem, cus);
+  if (small.waves > 0) {
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);
+    if (e == hipSuccess)
+      e = launch_down_small(fmt, small, static_cast<const uint8_t*>(a->w2), (int64_t)H * I * welem,
+                            fp8 ? static_cast<const void*>(qa) : abuf, ids, wts,
+                            fp8 ? a->w2_scale : nullptr, fp8 && !rows ? amax_a + kAmaxFinal : nullptr,
+                            rows ? sa : nullptr, P, K, H, I, a->out, stream);
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_COMBINE, stream);
+    if (e == hipSuccess) e = mark(ev, MOE_STAGE_COUNT, stream);
+    return hip_status(e);
+  }
   // a5
   if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);
   if (e == hipSuccess) {

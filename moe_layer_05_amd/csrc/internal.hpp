@@ -150,6 +150,22 @@ int tile_groups(int mode, int rows);
 hipError_t launch_gemm_tile(int mode, int fmt, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream);
 
+// Down product + combine in one launch for calls of at most 16 pairs
+// (down_small.hip); waves == 0 when the call does not fit (then the down
+// product and the combine launches run).  b_rows: bfloat16 a, or the FP8
+// codes of a with act_amax (the final amax word, per tensor) or act_scale
+// (one scale per pair row).
+struct SmallDownPlan {
+  int waves, region, depth;
+};
+SmallDownPlan small_down_plan(int64_t P, int K, int H, int I, int welem, int num_cus);
+hipError_t launch_down_small(int fmt, const SmallDownPlan& plan, const uint8_t* w2,
+                             int64_t w_expert_bytes, const void* b_rows, const int32_t* ids,
+                             const float* wts, const float* w_scale, const uint32_t* act_amax,
+                             const float* act_scale, int P, int K, int H, int I, void* out,
+                             hipStream_t stream);
+hipError_t prepare_down_small_kernels();
+
 // out[t] = bf16(sum over k, then parts, of w[t*K+k] * dw[part][t*K+k]); dw
 // float32, or bfloat16 when dw_bf16
 hipError_t launch_combine(const void* dw, bool dw_bf16, const float* w, int splits, int64_t T,
