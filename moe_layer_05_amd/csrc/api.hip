@@ -507,7 +507,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
   else if (e == hipSuccess && fp8)
     e = launch_quant_f32(fmt, static_cast<const float*>(abuf), (int64_t)P * I, amax_a, qa, cus,
                          stream);
-  // At most 16 pairs: the down product and the combine in one launch.
+  // At most 8 pairs: the down product and the combine in one launch.
   const SmallDownPlan small = L.tiled ? SmallDownPlan{} : small_down_plan(P, K, H, I, welem, cus);
   if (small.waves > 0) {
     if (e == hipSuccess) e = mark(ev, MOE_STAGE_DOWN, stream);

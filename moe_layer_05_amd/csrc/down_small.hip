@@ -1,13 +1,14 @@
-// a5 + a6 in one launch for calls of at most 16 token-expert pairs (one or
-// two decode tokens): the down product and the routing-weighted combine.
+// a5 + a6 in one launch for calls of at most 8 token-expert pairs (one decode
+// token at K <= 8, a few at smaller K): the down product and the
+// routing-weighted combine.
 //
 // The pages make the fused layer one pass over the selected experts whose
 // epilogue applies the scales and aggregates the experts' outputs (aib.vote
 // page, third paragraph), and single-token decode the shape where the fixed
 // work around the expert GEMMs weighs most (aib.vote page, second paragraph:
 // M < 64 or M = 1; toolboxkart.tech page, "Why MoE inference needs
-// specialized kernels").  With at most 16 pairs every pair fits one column of
-// a 16x16 MFMA tile, which lets one accumulator hold the down products of all
+// specialized kernels").  With so few pairs every pair fits one column of a
+// 16x16 MFMA tile, which lets one accumulator hold the down products of all
 // of a call's experts at once:
 //  - column p of the B operand holds pair p's intermediate row (bfloat16, or
 //    its FP8 codes); while the wave streams expert e's weight rows it zeroes
@@ -56,7 +57,7 @@ struct SmallDownArgs {
   uint16_t* out;              // [P / K][H] bfloat16
 };
 
-// NB: quarter token tiles (4 pair rows each) streamed per stage.  ROWS: FP8
+// NB: quarter token tiles (4 pair rows each) streamed per stage (1 or 2).  ROWS: FP8
 // with one scale per weight row and per pair row (else one per tensor).
 //
 // Work of a workgroup: steps t = c * nexp + j (chunk c of the row, j-th
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kSmallMaxWaves * kWave) void moe_down_small_kernel(
   constexpr bool FP8 = FMT != kFmtBF16;
   constexpr int kLoads = 4 + NB;                    // per stage: 16 weight rows, 4 * NB pair rows
   constexpr int kStage = kTileBytes + NB * 1024;
-  static_assert(NB == 1 || NB == 2 || NB == 4, "pair rows per stage");
+  static_assert(NB == 1 || NB == 2, "pair rows per stage");
   static_assert(!ROWS || FP8, "per-row scales are FP8 only");
   static_assert((kSmallD - 1) * kLoads <= 63, "ring deeper than the vmcnt counter");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(kSmallMaxWaves * kWave) void moe_down_small_kernel(
   uint8_t* ring = smem + (size_t)wave * p.region;
 
   // ---- the call's experts: lane p < P holds pair p's expert; lane j holds
-  // the j-th distinct expert in pair order (P <= 16)
+  // the j-th distinct expert in pair order (P <= 8)
   const int my_e = lane < p.P ? p.ids[lane] : -1;
   bool first = lane < p.P;
   for (int q = 0; q < 16; ++q) {
@@ -253,11 +254,10 @@ void launch_small(const SmallDownArgs& a, int nb, int nw, hipStream_t stream) {
   const dim3 grid(a.H / 16), block(nw * kWave);
   const size_t lds = (size_t)nw * a.region;
   if (nb == 1) moe_down_small_kernel<FMT, 1, ROWS><<<grid, block, lds, stream>>>(a);
-  else if (nb == 2) moe_down_small_kernel<FMT, 2, ROWS><<<grid, block, lds, stream>>>(a);
-  else moe_down_small_kernel<FMT, 4, ROWS><<<grid, block, lds, stream>>>(a);
+  else moe_down_small_kernel<FMT, 2, ROWS><<<grid, block, lds, stream>>>(a);
 }
 
-int stream_tiles(int P) { return P <= 4 ? 1 : P <= 8 ? 2 : 4; }
+int stream_tiles(int P) { return P <= 4 ? 1 : 2; }
 
 }  // namespace
 
@@ -268,7 +268,11 @@ int stream_tiles(int P) { return P <= 4 ? 1 : P <= 8 ? 2 : 4; }
 // wave are counted for the fewest experts a call can have (K).
 SmallDownPlan small_down_plan(int64_t P, int K, int H, int I, int welem, int num_cus) {
   SmallDownPlan best{};
-  if (P < 1 || P > 16 || K < 1 || P % K != 0 || H % 16 != 0 || I % 16 != 0) return best;
+  // up to 8 pairs: each stage's pair rows are then at most half its weight
+  // bytes (measured with 16 pairs, bf16 T = 8: 469 us per step against 442
+  // with the down product and combine launches -- the pair rows doubled each
+  // stage's L2 reads)
+  if (P < 1 || P > 8 || K < 1 || P % K != 0 || H % 16 != 0 || I % 16 != 0) return best;
   const int row_bytes = I * welem;
   const int nchunks = (row_bytes + kChunk - 1) / kChunk;
   const int stage = kTileBytes + stream_tiles((int)P) * 1024;
@@ -340,13 +344,10 @@ hipError_t launch_down_small(int fmt, const SmallDownPlan& plan, const uint8_t* 
 hipError_t prepare_down_small_kernels() {
   const hipError_t es[] = {
       ready_small<kFmtBF16, 1, false>(), ready_small<kFmtBF16, 2, false>(),
-      ready_small<kFmtBF16, 4, false>(), ready_small<kFmtE4M3, 1, false>(),
-      ready_small<kFmtE4M3, 2, false>(), ready_small<kFmtE4M3, 4, false>(),
+      ready_small<kFmtE4M3, 1, false>(), ready_small<kFmtE4M3, 2, false>(),
       ready_small<kFmtE4M3, 1, true>(),  ready_small<kFmtE4M3, 2, true>(),
-      ready_small<kFmtE4M3, 4, true>(),  ready_small<kFmtE5M2, 1, false>(),
-      ready_small<kFmtE5M2, 2, false>(), ready_small<kFmtE5M2, 4, false>(),
-      ready_small<kFmtE5M2, 1, true>(),  ready_small<kFmtE5M2, 2, true>(),
-      ready_small<kFmtE5M2, 4, true>()};
+      ready_small<kFmtE5M2, 1, false>(), ready_small<kFmtE5M2, 2, false>(),
+      ready_small<kFmtE5M2, 1, true>(),  ready_small<kFmtE5M2, 2, true>()};
   for (hipError_t e : es)
     if (e != hipSuccess) return e;
   return hipSuccess;

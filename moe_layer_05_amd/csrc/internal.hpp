@@ -150,7 +150,7 @@ int tile_groups(int mode, int rows);
 hipError_t launch_gemm_tile(int mode, int fmt, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream);
 
-// Down product + combine in one launch for calls of at most 16 pairs
+// Down product + combine in one launch for calls of at most 8 pairs
 // (down_small.hip); waves == 0 when the call does not fit (then the down
 // product and the combine launches run).  b_rows: bfloat16 a, or the FP8
 // codes of a with act_amax (the final amax word, per tensor) or act_scale

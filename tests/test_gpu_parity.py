@@ -497,7 +497,7 @@ def test_fused_fp8_prefill_zipf_sampled(wdtype):
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("over,T", [
-    (dict(H=2048, I=1040, E=16, K=4), 2),   # down product and combine in one launch
+    (dict(H=2048, I=1040, E=16, K=4), 2),   # down product and combine in one launch (8 pairs)
     (dict(H=2048, I=1040, E=16, K=4), 7),   # front launch (T <= 16)
     (dict(H=2048, I=1040, E=16, K=4), 40),  # router, act quant and align launches
     (dict(), 300),                          # tiled products
@@ -534,7 +534,7 @@ def test_fused_graph_replay_matches_eager(over, T, wdtype):
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8", "fp8row", "fp8e5"])
 @pytest.mark.parametrize("over,T", [
-    (dict(H=2048, I=1040, E=16, K=4), 2),   # down + combine launch, 8 waves per workgroup
+    (dict(H=2048, I=1040, E=16, K=4), 2),   # down + combine launch (8 pairs)
     (dict(H=2048, I=1040, E=16, K=4), 7),   # row tails in both products
     (dict(H=144, I=48, E=6, K=3), 40),
     (dict(), 300),
