@@ -124,12 +124,14 @@ __global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
 }
 
 // counts [C][E] -> exclusive offsets over the chunks (in place); seg [3][E]
-// receives the small and big segment starts and the per-expert totals.
+// receives the small and big segment starts and the per-expert totals;
+// n_clear words at `clear` are zeroed (the tiled products' work counters).
 __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
     int32_t* __restrict__ counts, int C, int E, int P, AlignOut small, AlignOut big, int thr,
-    int32_t* __restrict__ seg) {
+    int32_t* __restrict__ seg, uint32_t* __restrict__ clear, int n_clear) {
   __shared__ int wsum[2 * kAlignWaves];
   const int tid = threadIdx.x;
+  if (tid < n_clear) clear[tid] = 0u;
   int c_e = 0;
   if (tid < E) {
     constexpr int kBatch = 32;                       // loads in flight per thread
@@ -206,7 +208,10 @@ hipError_t launch_align_split_multi(const int32_t* ids, int P, int E, int BM_sma
                                     int32_t* sorted_small, int32_t* bexp_small,
                                     int32_t* npp_small, int BM_big, int32_t* sorted_big,
                                     int32_t* bexp_big, int32_t* npp_big, int thr, int32_t* rank,
-                                    int32_t* scratch, hipStream_t stream) {
+                                    int32_t* scratch, uint32_t* clear, int n_clear,
+                                    hipStream_t stream) {
+  if (n_clear < 0 || n_clear > kAlignThreads || (n_clear > 0 && clear == nullptr))
+    return hipErrorInvalidValue;
   AlignOut small{sorted_small, bexp_small, npp_small, BM_small};
   AlignOut big{sorted_big, bexp_big, npp_big, BM_big};
   const int C = (P + kAlignThreads - 1) / kAlignThreads;
@@ -216,7 +221,8 @@ hipError_t launch_align_split_multi(const int32_t* ids, int P, int E, int BM_sma
                                                                            rank);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  align_scan_kernel<<<1, kAlignThreads, 0, stream>>>(counts, C, E, P, small, big, thr, seg);
+  align_scan_kernel<<<1, kAlignThreads, 0, stream>>>(counts, C, E, P, small, big, thr, seg,
+                                                    clear, n_clear);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   align_scatter_kernel<<<C, kAlignThreads, 0, stream>>>(ids, P, E, counts, seg, rank, small, big,

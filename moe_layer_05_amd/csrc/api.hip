@@ -117,6 +117,7 @@ constexpr int64_t kRouterAmaxMaxBytes = 8 << 20;
 struct FusedLayout {
   size_t ids, wts, sorted, bexp, npp, rank, scal, srow, qx, a, qa, dw, ascr, total;
   size_t sorted_t, bexp_t, npp_t;     // tiled layout (prefill)
+  size_t tq;                          // tile counters of the two tiled products (2 x 8)
   int bm;
   int64_t cap, nblk;
   bool tiled;
@@ -174,6 +175,7 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, b
   L.sorted_t = take(L.tiled ? L.cap_t * 4 : 0);
   L.bexp_t = take(L.tiled ? L.nblk_t * 4 : 0);
   L.npp_t = take(4);
+  L.tq = take(L.tiled ? 16 * 4 : 0);
   L.rank = take(P * 4);
   L.ascr = take(L.tiled ? align_multi_workspace_bytes((int)P, E) : 0);
   L.scal = take(2 * kAmaxWords * 4);     // amax blocks of x and of a
@@ -455,7 +457,8 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       if (L.tiled)
         e = launch_align_split_multi(ids, P, E, L.bm, sorted, bexp, npp, tile_block_m(),
                                      sorted_t, bexp_t, npp_t, kTileThreshold, rank,
-                                     reinterpret_cast<int32_t*>(ws + L.ascr), stream);
+                                     reinterpret_cast<int32_t*>(ws + L.ascr),
+                                     reinterpret_cast<uint32_t*>(ws + L.tq), 16, stream);
       else if (quant_in_align)
         e = launch_align_quant(ids, P, E, L.bm, sorted, bexp, npp, rank, fmt, a->x, T, H, amax_x,
                                qx, rows ? sx : nullptr, cus, stream);
@@ -495,6 +498,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       t.block_expert = bexp_t;
       t.num_post_pad = npp_t;
       t.BM = tile_block_m();
+      t.tile_queue = reinterpret_cast<uint32_t*>(ws + L.tq);
       t.groups = tile_groups(kGateUp, I);
       t.splits = 1;
       e = launch_gemm_tile(kGateUp, fmt, t, L.nblk_t, cus, stream);
@@ -543,6 +547,7 @@ moe_status fused_forward_impl(const moe_fused_args* a, hipStream_t stream, hipEv
       t.block_expert = bexp_t;
       t.num_post_pad = npp_t;
       t.BM = tile_block_m();
+      t.tile_queue = reinterpret_cast<uint32_t*>(ws + L.tq) + 8;
       t.groups = tile_groups(kDown, H);
       t.splits = 1;
       e = launch_gemm_tile(kDown, fmt, t, L.nblk_t, cus, stream);

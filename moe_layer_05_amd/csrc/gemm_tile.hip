@@ -112,21 +112,30 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // Persistent: one workgroup per compute unit walks a list of tiles.  The
-  // routed blocks are cut into 8 contiguous ranges, one per XCD (workgroups
-  // are handed to the XCDs in turn, blockIdx & 7).  An XCD's tiles are walked
-  // in panels of 8 blocks x 4 column tiles and its workgroups take them in
-  // turn, so the 32 tiles running at once on an XCD read 8 token slices and 4
-  // weight slices per k-step from its L2 (measured 1.5% faster per prefill
-  // step than 4 x 8 with the weights loaded through the caches).
+  // Persistent: one workgroup per compute unit takes tiles until none is
+  // left.  The routed blocks are cut into 8 contiguous ranges, one per XCD
+  // (workgroups are handed to the XCDs in turn, blockIdx & 7), and each XCD's
+  // tiles form a list walked in panels of 8 blocks x 4 column tiles, so the
+  // 32 tiles running at once on an XCD read 8 token slices and 4 weight
+  // slices per k-step from its L2.  A workgroup takes the next tile of its
+  // XCD's list from an atomic counter, and once that list is empty the next
+  // tile of another XCD's list: the XCDs' lists cost different times (an
+  // expert with one block reads mostly padding token rows, which hit L2;
+  // measured per workgroup, static turns ended 846..1220 us into a 1220 us
+  // gate/up launch), so idle compute units take over the tail.  Every tile is
+  // taken exactly once and computed the same way by whichever workgroup, so
+  // the results do not depend on the schedule.
   constexpr int kPB = 8, kPN = 4;
   const int nb = p.num_post_pad[0] / kTN;
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, nj = gridDim.x >> 3;
-  const int b0 = (xcd * nb) >> 3, b1 = ((xcd + 1) * nb) >> 3;
-  const int cnt_x = (b1 - b0) * p.groups;
-  int it = j;
-  if (it >= cnt_x) return;                         // whole workgroup: before any barrier
-  auto tile_of = [&](int l, int& b, int& n) {
+  const int xcd = blockIdx.x & 7;
+  auto range = [&](int x, int& b0, int& b1) {
+    b0 = (x * nb) >> 3;
+    b1 = ((x + 1) * nb) >> 3;
+  };
+  // tile l of XCD x's list -> (block b, column tile n)
+  auto tile_of = [&](int x, int l, int& b, int& n) {
+    int b0, b1;
+    range(x, b0, b1);
     const int gw = p.groups;
     const int bp = l / (kPB * gw);
     const int bpw = min(kPB, (b1 - b0) - bp * kPB);
@@ -137,6 +146,20 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     b = b0 + bp * kPB + inner / npw;
     n = np * kPN + inner % npw;
   };
+  // the next tile as x << 24 | l, or -1 when every list is empty (one thread)
+  auto grab = [&]() -> int {
+    for (int d = 0; d < 8; ++d) {
+      const int x = (xcd + d) & 7;
+      int b0, b1;
+      range(x, b0, b1);
+      const int cnt = (b1 - b0) * p.groups;
+      if (cnt == 0) continue;
+      const int l = (int)atomicAdd(p.tile_queue + x, 1u);
+      if (l < cnt) return (x << 24) | l;
+    }
+    return -1;
+  };
+  __shared__ int s_next;
 
   const int row_bytes = (int)p.row_bytes;
   const int nfull = row_bytes / kBK;
@@ -160,9 +183,9 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   };
   const uint8_t* a_src[kLoadsPerWave];
   const uint8_t* b_src[kLoadsPerWave];
-  auto setup = [&](int l, Tile& s) {
+  auto setup = [&](int code, Tile& s) {
     int b;
-    tile_of(l, b, s.n);
+    tile_of(code >> 24, code & 0xFFFFFF, b, s.n);
     s.e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
     s.blk = p.sorted_ids + (int64_t)b * kTN;
     {
@@ -325,13 +348,18 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
 
   // ---- the walk: during a tile's last k-step the first stage of the next
   // tile is loaded, so a tile's start and its epilogue overlap with loads.
+  // The next tile is taken at a tile's first k-step (thread 0, into s_next)
+  // and read at its last, after the barriers between.
+  if (tid == 0) s_next = grab();
+  __syncthreads();
+  const int first = s_next;
+  if (first < 0) return;                           // uniform: every thread read s_next
   Tile cur, nxt;
-  setup(it, cur);
+  setup(first, cur);
   issue(0, 0);
   int stage = 0;
   for (;;) {
-    const int it_next = it + nj;
-    const bool has_next = it_next < cnt_x;
+    bool has_next = false;
 #pragma unroll
     for (int ai = 0; ai < 8; ++ai)
 #pragma unroll
@@ -339,11 +367,20 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     for (int k = 0; k < nk; ++k) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads of this stage
       __syncthreads();                                   // all waves: stage in, other stage read
+      if (k == 0) {
+        // every thread read s_next (the current tile) before this barrier
+        if (tid == 0) s_next = grab();
+        if (nk == 1) __syncthreads();
+      }
       if (k + 1 < nk) {
         issue(stage ^ 1, k + 1);
-      } else if (has_next) {
-        setup(it_next, nxt);
-        issue(stage ^ 1, 0);
+      } else {
+        const int next = s_next;
+        has_next = next >= 0;
+        if (has_next) {
+          setup(next, nxt);
+          issue(stage ^ 1, 0);
+        }
       }
       if (__builtin_amdgcn_readfirstlane(cur.nsub) > 0) compute(stage, k >= nfull, (uint32_t)k * kBK);
       stage ^= 1;
@@ -351,7 +388,6 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     epilogue(cur);
     if (!has_next) break;
     cur = nxt;
-    it = it_next;
   }
 }
 
@@ -388,7 +424,7 @@ int tile_groups(int mode, int rows) {
 
 hipError_t launch_gemm_tile(int mode, int fmt, const GemmParams& p, int64_t nblk_cap,
                             int num_cus, hipStream_t stream) {
-  if (p.BM != kTN) return hipErrorInvalidValue;
+  if (p.BM != kTN || p.tile_queue == nullptr) return hipErrorInvalidValue;
   const int64_t tiles = nblk_cap * p.groups;
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7FFFFFFF || p.row_bytes > (1 << 24)) return hipErrorInvalidValue;

@@ -40,6 +40,8 @@ struct GemmParams {
   int64_t dw_split_stride;     // elements between parts (P * H)
   int dw_bf16;                 // the partial rows are bfloat16 (prefill) instead of float32
   int H;
+  // tiled products: 8 work counters (one per XCD's tile list), zero at launch
+  uint32_t* tile_queue;
 };
 
 // Work decomposition of a decode GEMM launch (chosen on the host from the
@@ -85,13 +87,15 @@ hipError_t launch_front(const float* logits, int64_t T, int E, int K, int renorm
 
 // Two layouts at once (prefill), by three multi-workgroup launches: experts
 // with >= thr pairs in blocks of BM_big, the others in blocks of BM_small;
-// scratch holds align_multi_workspace_bytes(P, E).
+// scratch holds align_multi_workspace_bytes(P, E); the n_clear words at
+// `clear` are zeroed by the same launches (the tiled products' counters).
 size_t align_multi_workspace_bytes(int P, int E);
 hipError_t launch_align_split_multi(const int32_t* ids, int P, int E, int BM_small,
                                     int32_t* sorted_small, int32_t* bexp_small,
                                     int32_t* npp_small, int BM_big, int32_t* sorted_big,
                                     int32_t* bexp_big, int32_t* npp_big, int thr, int32_t* rank,
-                                    int32_t* scratch, hipStream_t stream);
+                                    int32_t* scratch, uint32_t* clear, int n_clear,
+                                    hipStream_t stream);
 
 hipError_t launch_zero_amax(uint32_t* p, int nblocks, hipStream_t stream);
 hipError_t launch_amax_bf16(const void* x, int64_t n, uint32_t* amax, int num_cus,
