@@ -137,6 +137,46 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int P, int E, Al
   }
 }
 
+// The same step by one wave for at most 64 pairs (the front launch of small
+// batches), with no LDS and no barrier: lane i holds pair i; its peers (the
+// lanes with the same expert) come from the same ballot multisplit, so its
+// rank among them is a popcount; the first lane of each expert knows the
+// expert's count and sums the padded counts of the experts with lower ids
+// (at most 64 of them) into the segment start.
+__device__ __forceinline__ void align_wave(const int32_t* ids, int P, int E, AlignOut out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int nbits = (E > 1) ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+  const bool valid = lane < P;
+  const int e = valid ? ids[lane] : 0;
+  uint64_t peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  const int rank = __popcll(peers & lt_mask);
+  const bool first = valid && rank == 0;
+  const int cnt = __popcll(peers);
+  const int pad = first ? (cnt + out.BM - 1) / out.BM * out.BM : 0;
+  int start = 0, total = 0;
+  const uint64_t firsts = __ballot(first);
+  for (uint64_t m = firsts; m; m &= m - 1) {       // uniform: every lane walks the experts
+    const int q = __builtin_ctzll(m);
+    const int eq = __shfl(e, q);
+    const int pq = __shfl(pad, q);
+    if (eq < e) start += pq;
+    total += pq;
+  }
+  const int seg = __shfl(start, valid ? __builtin_ctzll(peers) : 0);   // the expert's first lane
+  if (lane == 0) out.num_post_pad[0] = total;
+  if (first) {
+    for (int b = 0; b < pad / out.BM; ++b) out.block_expert[start / out.BM + b] = e;
+    for (int q = start + cnt; q < start + pad; ++q) out.sorted_ids[q] = P;
+  }
+  if (valid) out.sorted_ids[seg + rank] = lane;
+}
+
 // LDS of align_block: counts, segment starts, scan scratch (ints) and the
 // per-wave counts (bytes).
 constexpr size_t align_lds_words(int E) {

@@ -212,25 +212,6 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   }));
 }
 
-// max of 64-bit unsigned keys
-__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  auto step = [&](uint32_t olo, uint32_t ohi) {
-    const bool gt = ohi > hi || (ohi == hi && olo > lo);
-    lo = gt ? olo : lo;
-    hi = gt ? ohi : hi;
-  };
-  step(dpp::move<dpp::kSwap1, 0xF>(lo), dpp::move<dpp::kSwap1, 0xF>(hi));
-  step(dpp::move<dpp::kSwap2, 0xF>(lo), dpp::move<dpp::kSwap2, 0xF>(hi));
-  step(dpp::move<dpp::kHalfMirror, 0xF>(lo), dpp::move<dpp::kHalfMirror, 0xF>(hi));
-  step(dpp::move<dpp::kMirror, 0xF>(lo), dpp::move<dpp::kMirror, 0xF>(hi));
-  step(dpp::move<dpp::kBcast15, 0xA>(lo), dpp::move<dpp::kBcast15, 0xA>(hi));
-  step(dpp::move<dpp::kBcast31, 0xC>(lo), dpp::move<dpp::kBcast31, 0xC>(hi));
-  lo = (uint32_t)__builtin_amdgcn_readlane((int)lo, 63);
-  hi = (uint32_t)__builtin_amdgcn_readlane((int)hi, 63);
-  return ((uint64_t)hi << 32) | lo;
-}
-
 // ---------------------------------------------------------------- amax
 
 // A per-tensor amax is gathered in kAmaxSlots words, each on its own 128-byte

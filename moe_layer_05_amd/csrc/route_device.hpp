@@ -5,27 +5,14 @@
 // page, "Why MoE inference needs specialized kernels"; kongchang.com page, "Why
 // MoE Inference Is So Sensitive to Kernel Engineering").  The order is: larger
 // logit first, equal logits -> lower expert id.  Each lane holds up to
-// ceil(E/64) logits in registers; each of the K rounds takes a wave-wide
-// maximum of a 64-bit key (order-preserving float bits << 32 | ~expert id), so
-// the decision is exact on the float32 logits and ties resolve to the lower
-// id.  The winner's lane retires that logit.
+// ceil(E/64) logits in registers; each of the K rounds picks the largest
+// remaining logit and, among equal ones, the lowest id, with exact float32
+// comparisons.  The winner's lane retires that logit.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace moe {
-
-// Order-preserving map of float bits to uint32 (finite floats; -0 folded to +0
-// by the caller).
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(u);
-}
-
 
 // The logits of one token, lane l holding logits l, l + 64, ... (-0 folded
 // into +0; positions past E are 0 and never chosen).
@@ -41,7 +28,11 @@ __device__ __forceinline__ void load_logits(const float* __restrict__ row, int E
 
 // Routes one token from its loaded logits; lanes 0..K-1 write the chosen ids
 // and weights (softmax renormalised over the K, or over all E).  The whole
-// wave must be active.
+// wave must be active.  Each round takes the wave-wide maximum logit (a
+// 32-bit max over the lanes' own best), then the lowest expert id holding
+// it: one ballot when a single lane holds it, a 32-bit minimum of the ids
+// otherwise (ties: logits equal as floats, -0 already folded into +0) -- the
+// same choice as a maximum of the 64-bit key (logit, -id).
 template <int VPL>   // logits per lane: ceil(E / 64)
 __device__ __forceinline__ void route_values(const float (&v)[VPL], int E, int K, int renorm,
                                              int32_t* __restrict__ ids, float* __restrict__ wts) {
@@ -54,21 +45,30 @@ __device__ __forceinline__ void route_values(const float (&v)[VPL], int E, int K
   int my_id = 0;
   float my_val = 0.0f;
   for (int k = 0; k < K; ++k) {
-    uint64_t best = 0;                          // every finite key is > 0
+    // the lane's best: the largest of its available logits, the lowest id
+    // (smallest j) among equal ones; a lane with none offers -inf and no id
+    float lv = -__builtin_inff();
+    uint32_t le = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      if (avail & (1u << j)) {
-        uint32_t e = (uint32_t)(j * kWave + lane);
-        uint64_t key = ((uint64_t)order_key(v[j]) << 32) | (uint32_t)(~e);
-        best = key > best ? key : best;
+      if ((avail & (1u << j)) && (le == 0xFFFFFFFFu || v[j] > lv)) {
+        lv = v[j];
+        le = (uint32_t)(j * kWave + lane);
       }
     }
-    best = wave_max_u64_dpp(best);
-    uint32_t win = ~(uint32_t)best;
+    const float top = wave_max_dpp(lv);
+    const uint64_t cand = __ballot(le != 0xFFFFFFFFu && lv == top);
+    uint32_t win;
+    if (__popcll(cand) == 1) {
+      win = (uint32_t)__builtin_amdgcn_readlane((int)le, __builtin_ctzll(cand));
+    } else {
+      const uint32_t mine = ((cand >> lane) & 1) ? le : 0xFFFFFFFFu;
+      win = wave_reduce_dpp(mine, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    }
     if ((int)(win & (kWave - 1)) == lane) avail &= ~(1u << (win / kWave));
     if (k == lane) {
       my_id = (int)win;
-      my_val = key_value((uint32_t)(best >> 32));
+      my_val = top;
     }
   }
 
