@@ -138,12 +138,16 @@ __device__ __forceinline__ void align_block(const int32_t* ids, int P, int E, Al
 }
 
 // The same step by one wave for at most 64 pairs (the front launch of small
-// batches), with no LDS and no barrier: lane i holds pair i; its peers (the
-// lanes with the same expert) come from the same ballot multisplit, so its
-// rank among them is a popcount; the first lane of each expert knows the
-// expert's count and sums the padded counts of the experts with lower ids
-// (at most 64 of them) into the segment start.
-__device__ __forceinline__ void align_wave(const int32_t* ids, int P, int E, AlignOut out) {
+// batches), with no barrier: lane i holds pair i; its peers (the lanes with
+// the same expert) come from the same ballot multisplit, so its rank among
+// them is a popcount, and the first lane of each expert knows the expert's
+// count.  The segment starts are an exclusive scan of the padded counts over
+// the expert ids, through `lds` (E ints): lane l scans experts
+// [l * ceil(E/64), ...) and a wave prefix joins the lanes.  The padding is
+// written first, over every position, then the pairs over theirs (the two
+// store passes ordered by a wait).
+__device__ __forceinline__ void align_wave(const int32_t* ids, int P, int E, AlignOut out,
+                                           int* lds) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const int nbits = (E > 1) ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
@@ -158,22 +162,37 @@ __device__ __forceinline__ void align_wave(const int32_t* ids, int P, int E, Ali
   const int rank = __popcll(peers & lt_mask);
   const bool first = valid && rank == 0;
   const int cnt = __popcll(peers);
-  const int pad = first ? (cnt + out.BM - 1) / out.BM * out.BM : 0;
-  int start = 0, total = 0;
-  const uint64_t firsts = __ballot(first);
-  for (uint64_t m = firsts; m; m &= m - 1) {       // uniform: every lane walks the experts
-    const int q = __builtin_ctzll(m);
-    const int eq = __shfl(e, q);
-    const int pq = __shfl(pad, q);
-    if (eq < e) start += pq;
-    total += pq;
+  const int nblk = first ? (cnt + out.BM - 1) / out.BM : 0;   // blocks of expert e
+
+  // blocks per expert id in LDS, then their exclusive prefix over the ids
+  const int cpl = (E + kWave - 1) / kWave;
+  for (int i = 0; i < cpl; ++i) {
+    const int x = lane * cpl + i;
+    if (x < E) lds[x] = 0;
   }
-  const int seg = __shfl(start, valid ? __builtin_ctzll(peers) : 0);   // the expert's first lane
+  if (first) lds[e] = nblk;
+  int mine = 0;
+  for (int i = 0; i < cpl; ++i) {
+    const int x = lane * cpl + i;
+    if (x < E) mine += lds[x];
+  }
+  const int incl = wave_inclusive_sum_dpp(mine);
+  const int total = __builtin_amdgcn_readlane(incl, kWave - 1) * out.BM;
+  int run = incl - mine;
+  for (int i = 0; i < cpl; ++i) {
+    const int x = lane * cpl + i;
+    if (x < E) {
+      const int c = lds[x];
+      lds[x] = run;
+      run += c;
+    }
+  }
+  const int seg = lds[e] * out.BM;                 // valid lanes: their expert's start
   if (lane == 0) out.num_post_pad[0] = total;
-  if (first) {
-    for (int b = 0; b < pad / out.BM; ++b) out.block_expert[start / out.BM + b] = e;
-    for (int q = start + cnt; q < start + pad; ++q) out.sorted_ids[q] = P;
-  }
+  if (first)
+    for (int b = 0; b < nblk; ++b) out.block_expert[seg / out.BM + b] = e;
+  for (int q = lane; q < total; q += kWave) out.sorted_ids[q] = P;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the padding stores before the pairs'
   if (valid) out.sorted_ids[seg + rank] = lane;
 }
 

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kAlignThreads) void front_kernel(FrontArgs a) {
   const int P = a.T * a.K;
   if (tid < P) a.ids[tid] = s_ids[tid];
   if (P <= kWave) {
-    if (wave == 0) align_wave(s_ids, P, a.E, a.out);
+    if (wave == 0) align_wave(s_ids, P, a.E, a.out, smem);
   } else {
     align_block(s_ids, P, a.E, a.out, a.rank, smem);
   }
