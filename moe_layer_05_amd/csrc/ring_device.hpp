@@ -46,6 +46,81 @@ __device__ __forceinline__ void lds_read4(uint4 (&d)[4], uint32_t a0, uint32_t a
       : "memory");
 }
 
+// All NT tiles of one ring stage, tile t at byte offset t * kTileBytes from the
+// four MFMA-layout read addresses: up to three tiles (twelve reads) per asm
+// block, each block ending in its own wait (early-clobber outputs, as above).
+template <int T, int NT>
+__device__ __forceinline__ void lds_read_tiles(uint4 (&d)[NT][4], uint32_t a0, uint32_t a1,
+                                               uint32_t a2, uint32_t a3) {
+  if constexpr (T < NT) {
+    constexpr int rem = NT - T;
+    constexpr int n = (rem >= 3 && rem != 4) ? 3 : (rem >= 2 ? 2 : 1);
+    static_assert((T + n) * kTileBytes <= 65536, "LDS read offset range");
+    if constexpr (n == 3) {
+      asm volatile(
+          "ds_read_b128 %0, %12 offset:%16\n"
+          "ds_read_b128 %1, %13 offset:%16\n"
+          "ds_read_b128 %2, %14 offset:%16\n"
+          "ds_read_b128 %3, %15 offset:%16\n"
+          "ds_read_b128 %4, %12 offset:%17\n"
+          "ds_read_b128 %5, %13 offset:%17\n"
+          "ds_read_b128 %6, %14 offset:%17\n"
+          "ds_read_b128 %7, %15 offset:%17\n"
+          "ds_read_b128 %8, %12 offset:%18\n"
+          "ds_read_b128 %9, %13 offset:%18\n"
+          "ds_read_b128 %10, %14 offset:%18\n"
+          "ds_read_b128 %11, %15 offset:%18\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(d[T][0]), "=&v"(d[T][1]), "=&v"(d[T][2]), "=&v"(d[T][3]),
+            "=&v"(d[T + 1][0]), "=&v"(d[T + 1][1]), "=&v"(d[T + 1][2]), "=&v"(d[T + 1][3]),
+            "=&v"(d[T + 2][0]), "=&v"(d[T + 2][1]), "=&v"(d[T + 2][2]), "=&v"(d[T + 2][3])
+          : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(T * kTileBytes),
+            "n"((T + 1) * kTileBytes), "n"((T + 2) * kTileBytes)
+          : "memory");
+    } else if constexpr (n == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %8 offset:%12\n"
+          "ds_read_b128 %1, %9 offset:%12\n"
+          "ds_read_b128 %2, %10 offset:%12\n"
+          "ds_read_b128 %3, %11 offset:%12\n"
+          "ds_read_b128 %4, %8 offset:%13\n"
+          "ds_read_b128 %5, %9 offset:%13\n"
+          "ds_read_b128 %6, %10 offset:%13\n"
+          "ds_read_b128 %7, %11 offset:%13\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(d[T][0]), "=&v"(d[T][1]), "=&v"(d[T][2]), "=&v"(d[T][3]),
+            "=&v"(d[T + 1][0]), "=&v"(d[T + 1][1]), "=&v"(d[T + 1][2]), "=&v"(d[T + 1][3])
+          : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(T * kTileBytes), "n"((T + 1) * kTileBytes)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %4 offset:%8\n"
+          "ds_read_b128 %1, %5 offset:%8\n"
+          "ds_read_b128 %2, %6 offset:%8\n"
+          "ds_read_b128 %3, %7 offset:%8\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(d[T][0]), "=&v"(d[T][1]), "=&v"(d[T][2]), "=&v"(d[T][3])
+          : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "n"(T * kTileBytes)
+          : "memory");
+    }
+    lds_read_tiles<T + n, NT>(d, a0, a1, a2, a3);
+  }
+}
+
+// An empty asm that takes a tile's registers as read and written after every
+// memory operation before it: the products that use the tile cannot be
+// scheduled above loads issued before this point.
+__device__ __forceinline__ void after_issue(uint4 (&x)[4]) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  v4u t0 = __builtin_bit_cast(v4u, x[0]), t1 = __builtin_bit_cast(v4u, x[1]);
+  v4u t2 = __builtin_bit_cast(v4u, x[2]), t3 = __builtin_bit_cast(v4u, x[3]);
+  asm volatile("" : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3)::"memory");
+  x[0] = __builtin_bit_cast(uint4, t0);
+  x[1] = __builtin_bit_cast(uint4, t1);
+  x[2] = __builtin_bit_cast(uint4, t2);
+  x[3] = __builtin_bit_cast(uint4, t3);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
