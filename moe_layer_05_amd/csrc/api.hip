@@ -161,10 +161,11 @@ FusedLayout fused_layout(int64_t T, int H, int I, int E, int K, moe_wdtype wd, b
     L.nblk_t = P / bmt + big_experts;
     L.cap_t = L.nblk_t * bmt;
   }
-  L.gu = decode_shape(kGateUp, L.nblk, I, (int64_t)H * welem, L.bm, cus);
-  L.dn = decode_shape(kDown, L.nblk, H, (int64_t)I * welem, L.bm, cus);
+  const int64_t est = std::min<int64_t>(E, P);   // one block per active expert
+  L.gu = decode_shape(kGateUp, L.nblk, est, I, (int64_t)H * welem, L.bm, cus);
+  L.dn = decode_shape(kDown, L.nblk, est, H, (int64_t)I * welem, L.bm, cus);
   if (L.tiled) L.dn.splits = 1;          // the tiled products write one part
-  const int dw_parts = L.tiled ? 1 : decode_max_splits(L.nblk, H, (int64_t)I * welem);
+  const int dw_parts = L.tiled ? 1 : decode_max_splits(est, H, (int64_t)I * welem, L.bm);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes); return o; };
   L.ids = take(P * 4);

@@ -780,13 +780,22 @@ int64_t resident_waves(int ra, int nsub, int64_t row_bytes, int num_cus) {
   return (int64_t)std::max(num_cus, 1) * (per_cu > 0 ? per_cu : 1);
 }
 
+// Compute units the split rule counts at most: the largest gfx950 part, so
+// the workspace a call needs does not depend on the device.
+constexpr int kSplitCus = 256;
+
 // Parts of the down product's reduction for RA weight tiles per wave: split
-// while there are too few waves to cover the chip (about 2048 in flight),
-// keeping >= 8 chunks per part.
-int down_splits(int64_t nblk_cap, int rows, int nchunks, int ra) {
-  const int64_t units = nblk_cap * ((rows + 16 * ra - 1) / (16 * ra));
+// until the expected units (est_blocks routed blocks; the layout's capacity
+// holds more) give each resident wave about two, keeping >= 8 chunks per
+// part.  Measured on MI355X, bf16 H = 4096, I = 14336: 64 tokens (32-token
+// blocks) two parts 152 us, four 160 us, eight 183 us; 8 tokens one part
+// 195 us, two 144 us, four 149 us.
+int down_splits(int64_t est_blocks, int rows, int nchunks, int ra, int nsub, int64_t row_bytes,
+                int cus) {
+  const int64_t units = est_blocks * ((rows + 16 * ra - 1) / (16 * ra));
+  const int64_t resident = resident_waves(ra, nsub, row_bytes, std::min(cus, kSplitCus));
   int sp = 1;
-  while (units * sp < 2048 && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
+  while (units * sp < 2 * resident && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
   return sp;
 }
 
@@ -799,8 +808,8 @@ double round_fill(int64_t units, int64_t resident) {
 
 }  // namespace
 
-DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm,
-                         int num_cus) {
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int64_t est_blocks, int rows,
+                         int64_t row_bytes, int bm, int num_cus) {
   DecodeShape s{};
   const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
   const int nsub = bm / 16;
@@ -826,7 +835,9 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
   } else {
     // rows = H: RA 16-row tiles per wave; short rows take more tiles; the
     // reduction is split as down_splits says.
-    auto splits_of = [&](int ra) { return down_splits(nblk_cap, rows, nchunks, ra); };
+    auto splits_of = [&](int ra) {
+      return down_splits(est_blocks, rows, nchunks, ra, nsub, row_bytes, num_cus);
+    };
     auto units = [&](int ra) {
       return nblk_cap * ((rows + 16 * ra - 1) / (16 * ra)) * splits_of(ra);
     };
@@ -841,10 +852,11 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes
   return s;
 }
 
-int decode_max_splits(int64_t nblk_cap, int rows, int64_t row_bytes) {
+int decode_max_splits(int64_t est_blocks, int rows, int64_t row_bytes, int bm) {
   const int nchunks = (int)((row_bytes + kChunk - 1) / kChunk);
   int m = 1;
-  for (int ra : {2, 4, 8}) m = std::max(m, down_splits(nblk_cap, rows, nchunks, ra));
+  for (int ra : {2, 4, 8})
+    m = std::max(m, down_splits(est_blocks, rows, nchunks, ra, bm / 16, row_bytes, kSplitCus));
   return m;
 }
 

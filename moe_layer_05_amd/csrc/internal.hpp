@@ -138,12 +138,14 @@ hipError_t launch_inv_rope_quant(int fmt, bool interleaved, const void* x, int64
                                  int64_t T, int NH, int D, int R, uint8_t* codes, float* scales,
                                  int num_cus, hipStream_t stream);
 
-// The shape is chosen for num_cus compute units (the current device's).
-DecodeShape decode_shape(int mode, int64_t nblk_cap, int rows, int64_t row_bytes, int bm,
-                         int num_cus);
+// The shape is chosen for num_cus compute units (the current device's);
+// nblk_cap is the layout's block capacity, est_blocks the blocks a call
+// is expected to route (one per active expert).
+DecodeShape decode_shape(int mode, int64_t nblk_cap, int64_t est_blocks, int rows,
+                         int64_t row_bytes, int bm, int num_cus);
 // The most parts any shape choice splits the down product's reduction into,
 // whatever the device (bounds the workspace of the partial rows).
-int decode_max_splits(int64_t nblk_cap, int rows, int64_t row_bytes);
+int decode_max_splits(int64_t est_blocks, int rows, int64_t row_bytes, int bm);
 hipError_t launch_gemm_decode(int mode, int fmt, const GemmParams& p, int ra, int64_t nblk_cap,
                               int num_cus, hipStream_t stream);
 
