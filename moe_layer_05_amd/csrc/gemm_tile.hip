@@ -180,12 +180,18 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
     int n, e;
     const int32_t* blk;
     int nsub;                                      // 16-token tiles of this wave holding a pair
+    int rot;                                       // first k-step of the sweep
   };
   const uint8_t* a_src[kLoadsPerWave];
   const uint8_t* b_src[kLoadsPerWave];
   auto setup = [&](int code, Tile& s) {
     int b;
     tile_of(code >> 24, code & 0xFFFFFF, b, s.n);
+    // The tiles of XCD x's panels sweep the full k-steps from step
+    // x * nfull / 8 on, wrapping round (a partial last step stays last): the
+    // eight XCDs then read different column ranges at a time (measured on
+    // MI355X, FP8 Zipf T = 4096: gate/up stage 1457 -> 1443 us).
+    s.rot = (int)(((int64_t)(code >> 24) * nfull) / 8);
     s.e = __builtin_amdgcn_readfirstlane(p.block_expert[b]);
     s.blk = p.sorted_ids + (int64_t)b * kTN;
     {
@@ -211,9 +217,13 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
       b_src[i] = p.B + brow * row_bytes;
     }
   };
-  auto issue = [&](int stage, int k) {
-    const uint32_t off = (uint32_t)k * kBK;
+  auto issue = [&](int stage, int k, int rot) {
     const bool tail = k >= nfull;
+    if (!tail) {
+      k += rot;
+      if (k >= nfull) k -= nfull;
+    }
+    const uint32_t off = (uint32_t)k * kBK;
     const uint32_t o = (!tail || off + gq < (uint32_t)row_bytes) ? off + gq : 0u;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
@@ -356,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
   if (first < 0) return;                           // uniform: every thread read s_next
   Tile cur, nxt;
   setup(first, cur);
-  issue(0, 0);
+  issue(0, 0, cur.rot);
   int stage = 0;
   for (;;) {
     bool has_next = false;
@@ -373,13 +383,13 @@ __global__ __launch_bounds__(512, 1) void moe_gemm_tile_kernel(GemmParams p) {
         if (nk == 1) __syncthreads();
       }
       if (k + 1 < nk) {
-        issue(stage ^ 1, k + 1);
+        issue(stage ^ 1, k + 1, cur.rot);
       } else {
         const int next = s_next;
         has_next = next >= 0;
         if (has_next) {
           setup(next, nxt);
-          issue(stage ^ 1, 0);
+          issue(stage ^ 1, 0, nxt.rot);
         }
       }
       if (__builtin_amdgcn_readfirstlane(cur.nsub) > 0) compute(stage, k >= nfull, (uint32_t)k * kBK);
