@@ -29,7 +29,11 @@
 //    groups of an expert) go through the caches;
 //  - each wave owns a ring of D chunk stages in LDS and keeps D - 1 of them in
 //    flight; it waits on its own vector-memory counter, so no workgroup
-//    barrier is needed (one wave per workgroup);
+//    barrier is needed (one wave per workgroup); a stage is read into
+//    registers before its refill is issued, so the refill overlaps the
+//    stage's products;
+//  - gate/up waves start their sweep of the rows at different chunks, so the
+//    waves running at one time spread their reads over the rows' columns;
 //  - the unit of work is one wave: (block b, row group g, k-split s), where a
 //    row group is RA 16-row MFMA tiles; the grid is not persistent: one wave
 //    per unit of the capacity bound, so the hardware dispatcher balances the
