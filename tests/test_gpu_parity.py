@@ -426,11 +426,14 @@ def test_fused_shapes(over, wdtype):
 
 
 @pytest.mark.parametrize("wdtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("T", [1, 3])
+@pytest.mark.parametrize("T", [1, 3, 9, 20])
 def test_fused_split_reduction_ragged_tail(T, wdtype):
-    """A down product split into many parts over a row ending in a partial
-    chunk: bf16 I = 16400 is 129 chunks of 256 bytes, split 16 ways at T = 1;
-    every part is non-empty and only the last adds the partial chunk."""
+    """A down product over a row ending in a partial chunk: bf16 I = 16400 is
+    129 chunks of 256 bytes.  T = 1 and 3 (at most 8 pairs) take the launch
+    that does the down product and the combine together, streaming the whole
+    row; T = 9 (16-token blocks) and T = 20 (32-token blocks) take the decode
+    product split 16 ways, where every part is non-empty and only the last
+    adds the partial chunk."""
     cfg = replace(TINY, name="splitk", H=256, I=16400, E=2, K=1)
     run_case(cfg, T, wdtype)
 
