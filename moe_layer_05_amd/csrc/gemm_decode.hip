@@ -514,11 +514,11 @@ __global__ __launch_bounds__(64) void moe_gemm_stream_kernel(GemmParams p) {
             (const void*)(src[t][i] + o[i]),
             (lds_void*)(ring + (d * kTiles + t) * kTileBytes + i * 1024), 16, 0, 0);
   };
-  // issue the chunk of step t (into stage t % D), setting up its unit first
   // Gate/up units (one part per row) sweep their full chunks from position
   // unit mod the full-chunk count on, wrapping round, and read a partial last
   // chunk last: the same order as the one-wave-per-unit form.
   const int nrot = cps - (part_tail ? 1 : 0);
+  // issue the chunk of step t (into stage t % D), setting up its unit first
   auto issue_step = [&](int t) {
     const int k = t / cps, j = t - k * cps;
     if (j == 0) {
