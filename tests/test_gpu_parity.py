@@ -418,6 +418,8 @@ def test_fused_tiny(T, wdtype):
     dict(H=272, I=80, E=5, K=5),         # K = E
     dict(E=1, K=1),                      # one expert
     dict(H=2048, I=1040, E=16, K=4),     # several column tiles + a partial one
+    dict(H=2064, I=4096, E=8, K=2),      # gate/up in the persistent form (T = 7) over
+                                         # rows that end in a partial chunk
 ])
 def test_fused_shapes(over, wdtype):
     cfg = replace(TINY, name="tiny_" + "_".join(f"{k}{v}" for k, v in over.items()), **over)
