@@ -53,14 +53,30 @@
 namespace moe {
 namespace {
 
+// Rows of fewer chunks than this are short: their waves are short, and more
+// of them in flight wins (fewer weight tiles per wave, shallower rings).
+constexpr int kShortRow = 24;
+
 // Ring depth for RA weight tiles and NSUB token tiles per wave: each wave
-// holds D * (RA + NSUB) * 4 KB of LDS, and the depth is picked so the 160 KB of
-// a compute unit keep the most weight bytes in flight (waves per unit x
-// (D - 1) x RA x 4 KB), within the 6-bit vector-memory counter.
-constexpr int ring_depth(int ra, int nsub) {
-  return ra >= 8 ? 2
-                 : nsub == 1 ? (ra == 1 ? 5 : (ra == 2 ? 4 : 3))
-                             : (nsub == 2 ? (ra == 4 ? 3 : (ra == 2 ? 3 : 4)) : 2);
+// holds D * (RA + NSUB) * 4 KB of LDS, and 160 KB per compute unit.  A stage
+// is refilled as soon as it has been read, so nearly all D stages are loading
+// at any time, and shallow rings (more waves per compute unit) often measured
+// faster, though not for every shape (MI355X, per call):
+//  - one token tile, two weight tiles: short rows D = 2 (FP8 64 tokens down
+//    525 -> 512 us, TP8 slice 16 tokens gate/up 33 -> 31 us); long rows
+//    D = 3 for gate/up (bf16 8 tokens 284 -> 277 us) and 4 for the down
+//    product (bf16 32 tokens: D = 3 146 -> 154 us);
+//  - one token tile, four weight tiles: D = 2 for gate/up (FP8 1 token
+//    40.4 -> 39.2 us), 3 for the down product;
+//  - two token tiles, four weight tiles: D = 2 for gate/up (bf16 64 tokens
+//    298 -> 294 us), 3 for the down product (D = 2: 151 -> 159 us).
+// Within the 6-bit vector-memory counter.
+constexpr int ring_depth(int mode, int ra, int nsub, bool short_rows) {
+  return ra >= 8      ? 2
+         : nsub == 1  ? (ra == 2 ? (short_rows ? 2 : (mode == kGateUp ? 3 : 4))
+                                 : (mode == kGateUp ? 2 : 3))
+         : nsub == 2  ? (ra == 4 && mode == kGateUp ? 2 : 3)
+                      : 2;
 }
 
 template <int MODE, int FMT, int NSUB, int RA, int D>
@@ -698,6 +714,13 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
   return hipGetLastError();
 }
 
+// Rows of several chunks: both forms with the ring depth of the shape.
+template <int MODE, int FMT, int NSUB, int RA, bool SHORT>
+hipError_t launch_depth(const GemmParams& p, dim3 grid, int num_cus, hipStream_t stream) {
+  constexpr int D = ring_depth(MODE, RA, NSUB, SHORT);
+  return launch_best<MODE, FMT, NSUB, RA, D, D>(p, grid, num_cus, stream);
+}
+
 template <int MODE, int FMT, int RA>
 hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus,
                        hipStream_t stream) {
@@ -708,24 +731,32 @@ hipError_t launch_nsub(const GemmParams& p, int nsub_max, dim3 grid, int num_cus
     // one chunk per row: the one-wave-per-unit form needs no ring, so the LDS
     // holds more waves; the stream form keeps its ring across units
     switch (nsub_max) {
-      case 1: return launch_best<MODE, FMT, 1, RA, 1, ring_depth(RA, 1)>(p, grid, num_cus, stream);
-      case 2: return launch_best<MODE, FMT, 2, RA, 1, ring_depth(RA, 2)>(p, grid, num_cus, stream);
+      case 1:
+        return launch_best<MODE, FMT, 1, RA, 1, ring_depth(MODE, RA, 1, true)>(p, grid, num_cus,
+                                                                              stream);
+      case 2:
+        return launch_best<MODE, FMT, 2, RA, 1, ring_depth(MODE, RA, 2, true)>(p, grid, num_cus,
+                                                                              stream);
       case 4:
         if constexpr (RA < 8)
-          return launch_best<MODE, FMT, 4, RA, 1, ring_depth(RA, 4)>(p, grid, num_cus, stream);
+          return launch_best<MODE, FMT, 4, RA, 1, ring_depth(MODE, RA, 4, true)>(p, grid, num_cus,
+                                                                                 stream);
         return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
+  const bool sh = (p.row_bytes + kChunk - 1) / kChunk < kShortRow;
   switch (nsub_max) {
-    case 1: return launch_best<MODE, FMT, 1, RA, ring_depth(RA, 1), ring_depth(RA, 1)>(
-        p, grid, num_cus, stream);
-    case 2: return launch_best<MODE, FMT, 2, RA, ring_depth(RA, 2), ring_depth(RA, 2)>(
-        p, grid, num_cus, stream);
+    case 1:
+      return sh ? launch_depth<MODE, FMT, 1, RA, true>(p, grid, num_cus, stream)
+                : launch_depth<MODE, FMT, 1, RA, false>(p, grid, num_cus, stream);
+    case 2:
+      return sh ? launch_depth<MODE, FMT, 2, RA, true>(p, grid, num_cus, stream)
+                : launch_depth<MODE, FMT, 2, RA, false>(p, grid, num_cus, stream);
     case 4:
       if constexpr (RA < 8)
-        return launch_best<MODE, FMT, 4, RA, ring_depth(RA, 4), ring_depth(RA, 4)>(
-            p, grid, num_cus, stream);
+        return sh ? launch_depth<MODE, FMT, 4, RA, true>(p, grid, num_cus, stream)
+                  : launch_depth<MODE, FMT, 4, RA, false>(p, grid, num_cus, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -741,9 +772,14 @@ hipError_t launch_dtype(int fmt, const GemmParams& p, int nsub_max, dim3 grid, i
 
 template <int MODE, int FMT, int RA, int NSUB>
 hipError_t ready_shape() {
+  constexpr int DS = ring_depth(MODE, RA, NSUB, true), DL = ring_depth(MODE, RA, NSUB, false);
   hipError_t e = ready_one<MODE, FMT, NSUB, RA, 1>();
-  if (e == hipSuccess) e = ready_one<MODE, FMT, NSUB, RA, ring_depth(RA, NSUB)>();
-  if (e == hipSuccess) e = ready_stream<MODE, FMT, NSUB, RA, ring_depth(RA, NSUB)>();
+  if (e == hipSuccess) e = ready_one<MODE, FMT, NSUB, RA, DS>();
+  if (e == hipSuccess) e = ready_stream<MODE, FMT, NSUB, RA, DS>();
+  if constexpr (DL != DS) {
+    if (e == hipSuccess) e = ready_one<MODE, FMT, NSUB, RA, DL>();
+    if (e == hipSuccess) e = ready_stream<MODE, FMT, NSUB, RA, DL>();
+  }
   return e;
 }
 
@@ -778,8 +814,9 @@ namespace {
 
 // Waves of one shape that the chip holds at once: one wave per workgroup with
 // D * (RA + NSUB) 4 KB LDS tiles, 160 KB of LDS per compute unit.
-int64_t resident_waves(int ra, int nsub, int64_t row_bytes, int num_cus) {
-  const int d = row_bytes <= kChunk ? 1 : ring_depth(ra, nsub);
+int64_t resident_waves(int mode, int ra, int nsub, int64_t row_bytes, int num_cus) {
+  const bool sh = (row_bytes + kChunk - 1) / kChunk < kShortRow;
+  const int d = row_bytes <= kChunk ? 1 : ring_depth(mode, ra, nsub, sh);
   const int per_cu = (160 * 1024) / (d * (ra + nsub) * kTileBytes);
   return (int64_t)std::max(num_cus, 1) * (per_cu > 0 ? per_cu : 1);
 }
@@ -797,7 +834,7 @@ constexpr int kSplitCus = 256;
 int down_splits(int64_t est_blocks, int rows, int nchunks, int ra, int nsub, int64_t row_bytes,
                 int cus) {
   const int64_t units = est_blocks * ((rows + 16 * ra - 1) / (16 * ra));
-  const int64_t resident = resident_waves(ra, nsub, row_bytes, std::min(cus, kSplitCus));
+  const int64_t resident = resident_waves(kDown, ra, nsub, row_bytes, std::min(cus, kSplitCus));
   int sp = 1;
   while (units * sp < 2 * resident && nchunks / (2 * sp) >= 8 && sp < 16) sp *= 2;
   return sp;
@@ -822,10 +859,12 @@ DecodeShape decode_shape(int mode, int64_t nblk_cap, int64_t est_blocks, int row
   // round of resident waves costs a whole wave time, so the other RA is taken
   // when its grid fills the rounds clearly better (small grids).
   auto pick = [&](int pref, auto units_of) {
-    if (nchunks < 24) return 2;
+    if (nchunks < kShortRow) return 2;
     const int alt = 6 - pref;
-    const double fp = round_fill(units_of(pref), resident_waves(pref, nsub, row_bytes, num_cus));
-    const double fa = round_fill(units_of(alt), resident_waves(alt, nsub, row_bytes, num_cus));
+    const double fp =
+        round_fill(units_of(pref), resident_waves(mode, pref, nsub, row_bytes, num_cus));
+    const double fa =
+        round_fill(units_of(alt), resident_waves(mode, alt, nsub, row_bytes, num_cus));
     return fa > fp + 0.05 ? alt : pref;
   };
   if (mode == kGateUp) {
