@@ -79,6 +79,13 @@ constexpr int ring_depth(int mode, int ra, int nsub, bool short_rows) {
                       : 2;
 }
 
+// A grid that one round of waves with this deeper ring holds takes it: with
+// few waves the chip has room, and each wave's own loads in flight set the
+// pace (TP8 slice, 1 token, gate/up 96 waves: depth 4 11 us, depth 2 13 us).
+constexpr int deep_depth(int ra, int nsub) {
+  return ra >= 8 ? 2 : nsub == 1 ? (ra == 2 ? 4 : 3) : nsub == 2 ? 3 : 2;
+}
+
 template <int MODE, int FMT, int NSUB, int RA, int D>
 __global__ __launch_bounds__(64) void moe_gemm_decode_kernel(GemmParams p) {
   constexpr bool FP8 = FMT != kFmtBF16;
@@ -718,6 +725,11 @@ hipError_t launch_best(const GemmParams& p, dim3 grid, int num_cus, hipStream_t 
 template <int MODE, int FMT, int NSUB, int RA, bool SHORT>
 hipError_t launch_depth(const GemmParams& p, dim3 grid, int num_cus, hipStream_t stream) {
   constexpr int D = ring_depth(MODE, RA, NSUB, SHORT);
+  constexpr int DD = deep_depth(RA, NSUB);
+  if constexpr (DD > D) {
+    const int64_t deep = (int64_t)num_cus * ((160 * 1024) / (DD * (RA + NSUB) * kTileBytes));
+    if ((int64_t)grid.x <= deep) return launch_one<MODE, FMT, NSUB, RA, DD>(p, grid, stream);
+  }
   return launch_best<MODE, FMT, NSUB, RA, D, D>(p, grid, num_cus, stream);
 }
 
@@ -780,6 +792,9 @@ hipError_t ready_shape() {
     if (e == hipSuccess) e = ready_one<MODE, FMT, NSUB, RA, DL>();
     if (e == hipSuccess) e = ready_stream<MODE, FMT, NSUB, RA, DL>();
   }
+  constexpr int DD = deep_depth(RA, NSUB);
+  if constexpr (DD != DS && DD != DL)
+    if (e == hipSuccess) e = ready_one<MODE, FMT, NSUB, RA, DD>();
   return e;
 }
 
